@@ -1,0 +1,284 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact-attention backward on one MI355X.
+
+Workload: causal bf16 attention backward at B=8, H=16, N=4096, d=128 (the shape
+and FLOP convention of "Writing Speed-of-Light Attention Backward Kernel for
+5090 in CUDA", sections "Setup" and Appendix C), seeded synthetic N(0,1)
+inputs.  One timed step is the whole backward of the method: the preprocess
+D = rowsum(dO o O) plus the fused backward (dQ workspace clear, main kernel,
+dQ convert).  O and L come from this library's forward, run once before the
+timed region; the forward is also timed on its own and reported beside it.
+
+Prints ONE JSON line.  Effective TFLOPS = 10*B*H*N^2*d*(1/2 if causal) / time.
+
+    python bench.py [--steps K] [--warmup W] [--config headline|noncausal|...]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attn bwd effective TFLOPS (10·BHN²d·½ causal) & % bf16 MFMA peak, B8 H16 N4096 d128"
+PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 matrix peak (published)
+PEAK_HBM_GBS = 8000.0            # MI355X HBM3E (published)
+PAGES_BWD_TFLOPS = 160.06        # the pages' v3 backward at this workload (RTX 5090; context)
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "bwd_main_headline_counters.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_bwd_amd", "csrc", f)
+                  for f in ("attn_bwd.hip", "common.hpp")]
+
+
+# ----------------------------------------------------------------------------
+# FLOP / byte conventions (attention-backward page "Setup" and Appendix C;
+# the forward count is the 4*B*H*N^2*d of the flash_attention_cuda README table;
+# the sparse count 2*H*N*topk*(3*d_qk + 2*d_v) reproduces every row of the
+# cudnn-frontend PR #684 benchmark matrix)
+# ----------------------------------------------------------------------------
+def bwd_flops(B, H, N, d, causal):
+    f = 10.0 * B * H * N * N * d
+    return f * 0.5 if causal else f
+
+
+def fwd_flops(B, H, N, d, causal):
+    f = 4.0 * B * H * N * N * d
+    return f * 0.5 if causal else f
+
+
+def sparse_bwd_flops(H, N, topk, dqk, dv):
+    return 2.0 * H * N * topk * (3 * dqk + 2 * dv)
+
+
+def bwd_min_bytes(B, H, N, d):
+    """Read Q, K, V, O, dO (bf16) and L (fp32) once, write dQ, dK, dV (bf16) once."""
+    bhnd = B * H * N * d
+    return {"read": 5 * bhnd * 2 + B * H * N * 4, "write": 3 * bhnd * 2}
+
+
+def tflops(flops, ms):
+    return flops / (ms * 1e-3) / 1e12
+
+
+# ----------------------------------------------------------------------------
+# HIP events through the runtime PyTorch loaded (same process, same runtime)
+# ----------------------------------------------------------------------------
+class HipEvents:
+    def __init__(self):
+        self.rt = ctypes.CDLL("libamdhip64.so.7")
+        self.rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.rt.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        e = ctypes.c_void_p()
+        st = self.rt.hipEventCreate(ctypes.byref(e))
+        if st != 0:
+            raise RuntimeError(f"hipEventCreate failed: {st}")
+        return e.value
+
+    def elapsed_ms(self, a, b):
+        self.rt.hipEventSynchronize(ctypes.c_void_p(b))
+        ms = ctypes.c_float()
+        st = self.rt.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if st != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {st}")
+        return ms.value
+
+    def destroy(self, e):
+        self.rt.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def _sources_sha():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def _traffic():
+    """HBM bytes per launch of the main kernel from committed rocprofv3 counter
+    summaries, or None when they are absent or taken on a different source."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("source_sha256") != _sources_sha():
+        return None
+    return float(c["hbm_bytes_per_dispatch"])
+
+
+# ----------------------------------------------------------------------------
+def cpu_baseline(inp, cfg, budget_s):
+    """The fp64 oracle, timed on whole heads of the same workload."""
+    import numpy as np
+    import oracle
+    from attn_inputs import bf16_bits_to_f64
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    BH = cfg.B * cfg.H
+    per_head = bwd_flops(1, 1, cfg.N, cfg.d, cfg.causal)
+    done, t_total = 0, 0.0
+    while done < min(BH, 16) and (done == 0 or t_total < budget_s):
+        sl = lambda n: bf16_bits_to_f64(inp[n].reshape(BH, cfg.N, cfg.d)[done])  # noqa: E731
+        q, k, v, do = sl("q"), sl("k"), sl("v"), sl("do")
+        t0 = time.perf_counter()
+        oracle.attention_backward(q, k, v, do, cfg.scale, causal=cfg.causal)
+        t_total += time.perf_counter() - t0
+        done += 1
+    return {
+        "value": round(tflops(per_head * done, t_total * 1e3), 6),
+        "unit": "TFLOPS",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"fp64 numpy forward+backward of {done} of {BH} heads "
+                  f"(N={cfg.N}, d={cfg.d}, causal={cfg.causal}), {t_total:.1f} s",
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="headline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(--gpus {args.gpus} is not supported)", file=sys.stderr)
+        return 2
+
+    import torch
+    import exact_attention_bwd_amd as ea
+    from attn_inputs import DENSE_CONFIGS, make_dense_inputs
+
+    cfg = DENSE_CONFIGS[args.config]
+    B, H, N, d = cfg.B, cfg.H, cfg.N, cfg.d
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] {cfg.name}: B{B} H{H} N{N} d{d} causal={cfg.causal}", file=sys.stderr, flush=True)
+
+    inp = make_dense_inputs(cfg)
+    import numpy as np
+
+    def up(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v, do = (up(inp[n]) for n in ("q", "k", "v", "do"))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    D = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty((ea.attn_bwd_workspace_bytes(B, H, N, d),), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    ev = HipEvents()
+
+    ea.attn_fwd(q, k, v, cfg.causal, cfg.scale, o=o, lse=lse)
+    torch.cuda.synchronize()
+
+    def step(events=None):
+        ea.attn_bwd_preprocess(o, do, D=D)
+        ea.attn_bwd(q, k, v, do, lse, D, cfg.causal, cfg.scale, dq=dq, dk=dk, dv=dv,
+                    workspace=ws, main_events=events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup {args.warmup} done", file=sys.stderr, flush=True)
+
+    K = args.steps
+    pairs = [(ev.create(), ev.create()) for _ in range(K)]
+    t0, t1 = ev.create(), ev.create()
+    torch.cuda.synchronize()
+    ev.rt.hipEventRecord(ctypes.c_void_p(t0), ctypes.c_void_p(stream.cuda_stream))
+    for i in range(K):
+        step(pairs[i])
+    ev.rt.hipEventRecord(ctypes.c_void_p(t1), ctypes.c_void_p(stream.cuda_stream))
+    torch.cuda.synchronize()
+    total_ms = ev.elapsed_ms(t0, t1)
+    main_ms = [ev.elapsed_ms(a, b) for a, b in pairs]
+    ms_step = total_ms / K
+    main_avg = sum(main_ms) / K
+    print(f"[bench] timed {K} steps: {ms_step:.4f} ms/step, main kernel {main_avg:.4f} ms",
+          file=sys.stderr, flush=True)
+
+    # forward, timed on its own (not part of the metric)
+    for _ in range(max(2, args.warmup // 2)):
+        ea.attn_fwd(q, k, v, cfg.causal, cfg.scale, o=o, lse=lse)
+    torch.cuda.synchronize()
+    ev.rt.hipEventRecord(ctypes.c_void_p(t0), ctypes.c_void_p(stream.cuda_stream))
+    for _ in range(K):
+        ea.attn_fwd(q, k, v, cfg.causal, cfg.scale, o=o, lse=lse)
+    ev.rt.hipEventRecord(ctypes.c_void_p(t1), ctypes.c_void_p(stream.cuda_stream))
+    torch.cuda.synchronize()
+    fwd_ms = ev.elapsed_ms(t0, t1) / K
+    for a, b in pairs:
+        ev.destroy(a)
+        ev.destroy(b)
+    ev.destroy(t0)
+    ev.destroy(t1)
+
+    fl = bwd_flops(B, H, N, d, cfg.causal)
+    value = tflops(fl, ms_step)
+    main_tf = tflops(fl, main_avg)
+    traffic = _traffic()
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(value / PAGES_BWD_TFLOPS, 4) if cfg.name == "headline" else None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{'causal' if cfg.causal else 'non-causal'} attention backward "
+                        f"(preprocess + fused backward) B{B} H{H} N{N} d{d} bf16, seed {cfg.seed}",
+            "B": B, "H": H, "N": N, "d": d, "causal": cfg.causal, "scale": cfg.scale,
+        },
+        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 3),
+        "peak_tflops": PEAK_BF16_TFLOPS,
+        "flops_per_step": fl,
+        "main_kernel": {"ms": round(main_avg, 5), "tflops": round(main_tf, 3),
+                        "ms_min": round(min(main_ms), 5), "ms_max": round(max(main_ms), 5)},
+        "forward": {"ms": round(fwd_ms, 5),
+                    "tflops": round(tflops(fwd_flops(B, H, N, d, cfg.causal), fwd_ms), 3)},
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "bwd_main_kernel",
+            "achieved": round(main_tf, 3),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(main_tf / PEAK_BF16_TFLOPS, 5),
+            "traffic": traffic,
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(inp, cfg, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

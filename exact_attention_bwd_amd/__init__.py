@@ -1,0 +1,175 @@
+"""Python binding of the MI355X exact-attention library (``libattn_mi355x.so``).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/attn_mi355x.h``.  PyTorch is
+used for device memory and the current stream.  There is no fallback: if the
+shared library is missing or fails to load, importing this package raises.
+
+The library is loaded after ``import torch`` so that it binds to the HIP
+runtime PyTorch already loaded (same soname), giving one runtime per process.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = [
+    "attn_fwd", "attn_bwd_preprocess", "attn_bwd", "attn_bwd_workspace_bytes",
+    "attention_backward", "lib_path", "AttnError", "version",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libattn_mi355x.so")
+
+
+class AttnError(RuntimeError):
+    """A non-OK status returned by the C ABI."""
+
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"attn status {status}: {msg}")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(lib_path):
+        raise ImportError(
+            f"{lib_path} is missing: build it first (python -m exact_attention_bwd_amd.build)")
+    lib = ctypes.CDLL(lib_path, mode=ctypes.RTLD_GLOBAL)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+    lib.attn_fwd.restype = i
+    lib.attn_bwd_preprocess.argtypes = [vp, vp, vp, i, i, i, i, vp]
+    lib.attn_bwd_preprocess.restype = i
+    lib.attn_bwd_workspace_bytes.argtypes = [i, i, i, i]
+    lib.attn_bwd_workspace_bytes.restype = sz
+    lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, vp]
+    lib.attn_bwd.restype = i
+    lib.attn_bwd_timed.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, vp, vp, vp]
+    lib.attn_bwd_timed.restype = i
+    lib.attn_last_error.argtypes = []
+    lib.attn_last_error.restype = ctypes.c_char_p
+    lib.attn_version.argtypes = []
+    lib.attn_version.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = _load()
+
+
+def version() -> str:
+    return _lib.attn_version().decode()
+
+
+def _check(status: int):
+    if status != 0:
+        raise AttnError(status, _lib.attn_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _shape4(x: torch.Tensor, name: str):
+    if x.dim() != 4:
+        raise ValueError(f"{name} must be [B, H, N, d], got {tuple(x.shape)}")
+    if x.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {x.dtype}")
+    if not x.is_cuda or not x.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous device tensor")
+    return tuple(x.shape)
+
+
+def _same(shape, x: torch.Tensor, name: str):
+    if _shape4(x, name) != shape:
+        raise ValueError(f"{name} has shape {tuple(x.shape)}, expected {shape}")
+
+
+def _stat(x: torch.Tensor, shape3, name: str):
+    if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous() or tuple(x.shape) != shape3:
+        raise ValueError(f"{name} must be a contiguous float32 device tensor of shape {shape3}")
+
+
+def attn_fwd(q, k, v, causal: bool, scale: float | None = None, o=None, lse=None, stream=None):
+    """Forward pass.  q, k, v: bf16 [B, H, N, d].  Returns (o bf16, lse fp32 [B, H, N])."""
+    shape = _shape4(q, "q")
+    _same(shape, k, "k")
+    _same(shape, v, "v")
+    B, H, N, d = shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if o is None:
+        o = torch.empty_like(q)
+    _same(shape, o, "o")
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _stat(lse, (B, H, N), "lse")
+    _check(_lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
+                         int(bool(causal)), float(scale), _stream(stream)))
+    return o, lse
+
+
+def attn_bwd_preprocess(o, do, D=None, stream=None):
+    """D = rowsum(dO o O) in fp32, shape [B, H, N]."""
+    shape = _shape4(o, "o")
+    _same(shape, do, "dO")
+    B, H, N, d = shape
+    if D is None:
+        D = torch.empty((B, H, N), dtype=torch.float32, device=o.device)
+    _stat(D, (B, H, N), "D")
+    _check(_lib.attn_bwd_preprocess(_ptr(o), _ptr(do), _ptr(D), B, H, N, d, _stream(stream)))
+    return D
+
+
+def attn_bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    return int(_lib.attn_bwd_workspace_bytes(B, H, N, d))
+
+
+def attn_bwd(q, k, v, do, lse, D, causal: bool, scale: float | None = None,
+             dq=None, dk=None, dv=None, workspace=None, stream=None, main_events=None):
+    """Fused backward.  Returns (dq, dk, dv), bf16 [B, H, N, d].
+
+    ``main_events``: optional pair of raw hipEvent_t handles (ints) recorded on
+    the stream around the fused main kernel (profiling; see attn_bwd_timed)."""
+    shape = _shape4(q, "q")
+    for t, n in ((k, "k"), (v, "v"), (do, "dO")):
+        _same(shape, t, n)
+    B, H, N, d = shape
+    _stat(lse, (B, H, N), "lse")
+    _stat(D, (B, H, N), "D")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _same(shape, t, n)
+    need = attn_bwd_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    if main_events is None:
+        _check(_lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(D), _ptr(dq),
+                             _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, B, H, N, d,
+                             int(bool(causal)), float(scale), _stream(stream)))
+    else:
+        ev0, ev1 = (ctypes.c_void_p(e) for e in main_events)
+        _check(_lib.attn_bwd_timed(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(D), _ptr(dq),
+                                   _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, B, H, N, d,
+                                   int(bool(causal)), float(scale), _stream(stream), ev0, ev1))
+    return dq, dk, dv
+
+
+def attention_backward(q, k, v, do, o, lse, causal: bool, scale: float | None = None,
+                       workspace=None, stream=None):
+    """The whole backward of the method: preprocess (D) then the fused backward."""
+    D = attn_bwd_preprocess(o, do, stream=stream)
+    return attn_bwd(q, k, v, do, lse, D, causal, scale, workspace=workspace, stream=stream)

@@ -1,0 +1,137 @@
+// C entry points of the attention library: argument validation, then the
+// launchers.  No allocation, no synchronisation, no exceptions across the ABI.
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "../../include/attn_mi355x.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+attn_status fail(attn_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+attn_status ok() {
+    g_err[0] = '\0';
+    return ATTN_OK;
+}
+
+attn_status hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(ATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Common shape checks.  Sets *empty when there is nothing to do.
+attn_status check_shape(int B, int H, int N, int d, bool* empty) {
+    if (B < 0 || H < 0 || N < 0) return fail(ATTN_ERR_INVALID_ARG, "negative size B=%d H=%d N=%d", B, H, N);
+    if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dimension d=%d not in {64, 128}", d);
+    const long long bh = (long long)B * H;
+    *empty = (bh * N == 0);
+    if (*empty) return ATTN_OK;
+    // grid and index limits: B*H*ceil(N/64) workgroups, B*H*N rows, element offsets in 64 bits
+    if (bh > (1LL << 24) || N > (1 << 26) || bh * (((long long)N + 63) / 64) > 0x7fffffffLL)
+        return fail(ATTN_ERR_UNSUPPORTED, "sizes too large B*H=%lld N=%d", bh, N);
+    return ATTN_OK;
+}
+
+attn_status check_ptr(const void* p, const char* name, uintptr_t align) {
+    if (p == nullptr) return fail(ATTN_ERR_INVALID_ARG, "%s is NULL", name);
+    if (!aligned(p, align)) return fail(ATTN_ERR_INVALID_ARG, "%s is not %u-byte aligned", name, (unsigned)align);
+    return ATTN_OK;
+}
+
+#define CHECK(expr)                         \
+    do {                                    \
+        attn_status _s = (expr);            \
+        if (_s != ATTN_OK) return _s;       \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                     int H, int N, int d, int causal, float scale, void* stream) {
+    bool empty = false;
+    CHECK(check_shape(B, H, N, d, &empty));
+    if (!isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "scale is not finite");
+    if (empty) return ok();
+    CHECK(check_ptr(q, "q", 16));
+    CHECK(check_ptr(k, "k", 16));
+    CHECK(check_ptr(v, "v", 16));
+    CHECK(check_ptr(o, "o", 16));
+    CHECK(check_ptr(lse, "lse", 4));
+    return hip_status(attn::launch_fwd(q, k, v, o, lse, B * H, N, d, causal != 0, scale,
+                                       (hipStream_t)stream),
+                      "attn_fwd launch");
+}
+
+attn_status attn_bwd_preprocess(const void* o, const void* dO, float* D, int B, int H, int N,
+                                int d, void* stream) {
+    bool empty = false;
+    CHECK(check_shape(B, H, N, d, &empty));
+    if (empty) return ok();
+    CHECK(check_ptr(o, "o", 16));
+    CHECK(check_ptr(dO, "dO", 16));
+    CHECK(check_ptr(D, "D", 4));
+    return hip_status(attn::launch_bwd_preprocess(o, dO, D, B * H, N, d, (hipStream_t)stream),
+                      "attn_bwd_preprocess launch");
+}
+
+size_t attn_bwd_workspace_bytes(int B, int H, int N, int d) {
+    bool empty = false;
+    if (check_shape(B, H, N, d, &empty) != ATTN_OK || empty) return 0;
+    return attn::bwd_workspace_bytes(B * H, N, d);
+}
+
+attn_status attn_bwd_timed(const void* q, const void* k, const void* v, const void* dO,
+                     const float* lse, const float* D, void* dq, void* dk, void* dv,
+                     void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                     int causal, float scale, void* stream, void* main_start, void* main_stop) {
+    bool empty = false;
+    CHECK(check_shape(B, H, N, d, &empty));
+    if (!isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "scale is not finite");
+    if (empty) return ok();
+    CHECK(check_ptr(q, "q", 16));
+    CHECK(check_ptr(k, "k", 16));
+    CHECK(check_ptr(v, "v", 16));
+    CHECK(check_ptr(dO, "dO", 16));
+    CHECK(check_ptr(lse, "lse", 4));
+    CHECK(check_ptr(D, "D", 4));
+    CHECK(check_ptr(dq, "dq", 16));
+    CHECK(check_ptr(dk, "dk", 16));
+    CHECK(check_ptr(dv, "dv", 16));
+    CHECK(check_ptr(workspace, "workspace", 16));
+    const size_t need = attn::bwd_workspace_bytes(B * H, N, d);
+    if (workspace_bytes < need)
+        return fail(ATTN_ERR_WORKSPACE, "workspace is %zu bytes, %zu needed", workspace_bytes, need);
+    return hip_status(attn::launch_bwd(q, k, v, dO, lse, D, dq, dk, dv, workspace, B * H, N, d,
+                                       causal != 0, scale, (hipStream_t)stream,
+                                       (hipEvent_t)main_start, (hipEvent_t)main_stop),
+                      "attn_bwd launch");
+}
+
+attn_status attn_bwd(const void* q, const void* k, const void* v, const void* dO,
+                     const float* lse, const float* D, void* dq, void* dk, void* dv,
+                     void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                     int causal, float scale, void* stream) {
+    return attn_bwd_timed(q, k, v, dO, lse, D, dq, dk, dv, workspace, workspace_bytes, B, H, N, d,
+                          causal, scale, stream, nullptr, nullptr);
+}
+
+const char* attn_last_error(void) { return g_err; }
+
+const char* attn_version(void) { return "attn_mi355x 0.1 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,123 @@
+/*
+ * attn_mi355x.h -- C ABI of the exact-attention library for AMD MI355X (gfx950).
+ *
+ * Fused exact scaled-dot-product attention, FlashAttention-2 style: a forward
+ * pass that emits O and the row log-sum-exp L, the backward preprocess
+ * D = rowsum(dO o O), and the fused backward producing dQ, dK and dV.
+ *
+ * The operations are those of "Writing Speed-of-Light Attention Backward Kernel
+ * for 5090 in CUDA" (hoanh.space), section "Mathematical Formulation":
+ *     S  = scale * Q K^T + M            (M = 0, or -inf where key j > query i when causal)
+ *     L_i = log sum_j exp(S_ij)          (natural log, of the scaled masked scores)
+ *     P  = exp(S - L),  O = P V
+ *     dV = P^T dO,  dP = dO V^T,  D = rowsum(dO o O),  dS = P o (dP - D 1^T)
+ *     dQ = scale * dS K,  dK = scale * dS^T Q
+ * The page writes scale = 1/sqrt(d); here it is an argument.
+ *
+ * Conventions shared by every entry point
+ *  - Tensors are dense, row-major, [B, H, N, d] (d fastest), bf16 unless noted;
+ *    L and D are fp32 [B, H, N].  Pointers are device pointers (memory from
+ *    hipMalloc or a framework allocator on the current device).
+ *  - bf16 pointers must be 16-byte aligned; fp32 pointers 4-byte aligned; the
+ *    workspace 16-byte aligned.
+ *  - d must be 64 or 128.  N >= 1 may be any length (a ragged last tile is
+ *    masked).  B*H*N == 0 is a no-op that returns ATTN_OK.
+ *  - The caller owns every buffer, including the workspace.  The library never
+ *    allocates, frees or synchronises: all work is enqueued on `stream`
+ *    (a hipStream_t; NULL = the default stream) and ATTN_OK means the launches
+ *    were enqueued, not that they have finished.
+ *  - Errors are returned, never thrown.  On a non-OK status nothing was
+ *    enqueued (validation errors) or the HIP launch failed (ATTN_ERR_HIP);
+ *    attn_last_error() returns a message for the calling thread.
+ *  - Calls may run concurrently on different streams if their output and
+ *    workspace buffers do not overlap.
+ */
+#ifndef ATTN_MI355X_H
+#define ATTN_MI355X_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int attn_status;
+
+#define ATTN_OK 0
+#define ATTN_ERR_INVALID_ARG (-1)   /* null/misaligned pointer, negative size, non-finite scale */
+#define ATTN_ERR_UNSUPPORTED (-2)   /* head dimension not in {64, 128}, sizes too large */
+#define ATTN_ERR_HIP (-3)           /* a HIP launch or attribute call failed */
+#define ATTN_ERR_WORKSPACE (-4)     /* workspace smaller than attn_bwd_workspace_bytes() */
+
+/*
+ * Forward pass (tiled online softmax; s-samchenko/flash_attention_cuda README,
+ * FlashAttention-2 forward with running max m, normaliser l and rescale by
+ * exp(m_old - m_new)).
+ *   q, k, v : bf16 [B, H, N, d], read only
+ *   o       : bf16 [B, H, N, d], written (O = P V, rounded to nearest even)
+ *   lse     : fp32 [B, H, N], written: L_i, natural log of sum_j exp(S_ij)
+ *   causal  : nonzero = key j visible to query i only if j <= i
+ *   scale   : softmax scale applied to Q K^T (finite)
+ */
+attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                     int H, int N, int d, int causal, float scale, void* stream);
+
+/*
+ * Backward preprocess (attention-backward page, section "Precomputing D"):
+ *   D_i = sum_c dO_ic * O_ic, accumulated in fp32 from the bf16 inputs.
+ *   o, dO : bf16 [B, H, N, d], read only;  D : fp32 [B, H, N], written.
+ */
+attn_status attn_bwd_preprocess(const void* o, const void* dO, float* D, int B, int H, int N,
+                                int d, void* stream);
+
+/*
+ * Size in bytes of the workspace attn_bwd needs (an fp32 dQ accumulator with
+ * the sequence rounded up to the 64-row query tile).  0 when B*H*N == 0.
+ */
+size_t attn_bwd_workspace_bytes(int B, int H, int N, int d);
+
+/*
+ * Fused backward (attention-backward page: the tiled backward pseudocode and
+ * section "Main backward kernel"): recomputes P = exp(scale*S - L) tile by tile
+ * and forms dV = P^T dO, dP = dO V^T, dS = P o (dP - D), dQ = scale*dS K and
+ * dK = scale*dS^T Q.  dQ partials are added in fp32 into `workspace`
+ * (cleared by this call) and rounded to bf16 by a second kernel on the same
+ * stream.
+ *   q, k, v, dO : bf16 [B, H, N, d], read only
+ *   lse         : fp32 [B, H, N]  L from attn_fwd (natural log), read only
+ *   D           : fp32 [B, H, N]  from attn_bwd_preprocess, read only
+ *   dq, dk, dv  : bf16 [B, H, N, d], written
+ *   workspace   : device scratch of at least attn_bwd_workspace_bytes(B,H,N,d)
+ *                 bytes (its content on entry is ignored and on exit unspecified)
+ *   causal, scale : as for attn_fwd (must match the forward that produced lse)
+ * dQ is reduced with fp32 atomics, so its low-order bits may differ between
+ * runs; dK and dV are deterministic.
+ */
+attn_status attn_bwd(const void* q, const void* k, const void* v, const void* dO,
+                     const float* lse, const float* D, void* dq, void* dk, void* dv,
+                     void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                     int causal, float scale, void* stream);
+
+/*
+ * Same as attn_bwd, for profiling: when main_start / main_stop (hipEvent_t
+ * created by the caller) are non-NULL they are recorded on `stream`
+ * immediately before and after the fused backward kernel, so the caller can
+ * time that kernel alone (hipEventElapsedTime) without a profiler.
+ */
+attn_status attn_bwd_timed(const void* q, const void* k, const void* v, const void* dO,
+                           const float* lse, const float* D, void* dq, void* dk, void* dv,
+                           void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                           int causal, float scale, void* stream, void* main_start,
+                           void* main_stop);
+
+/* Message describing the last non-OK status returned on this thread ("" if none). */
+const char* attn_last_error(void);
+
+/* Library version string. */
+const char* attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_MI355X_H */

@@ -1,0 +1,97 @@
+"""The C ABI library loads, exports every symbol its header declares, and its
+argument validation returns the documented status codes.  None of these calls
+launches anything, so they run without a GPU."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_mi355x.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:attn_status|size_t|const char\*)\s+(attn_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def ea():
+    import exact_attention_bwd_amd as ea
+    return ea
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ("attn_fwd", "attn_bwd_preprocess", "attn_bwd", "attn_bwd_workspace_bytes", "attn_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(ea):
+    out = subprocess.run(["nm", "-D", "--defined-only", ea.lib_path], capture_output=True, text=True, check=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    missing = [n for n in _declared() if n not in exported]
+    assert not missing, missing
+    lib = ctypes.CDLL(ea.lib_path)
+    for n in _declared():
+        assert getattr(lib, n) is not None
+
+
+def test_library_is_gfx950_code(ea):
+    out = subprocess.run(["strings", ea.lib_path], capture_output=True, text=True, check=True).stdout
+    assert "gfx950" in out
+
+
+def test_workspace_size(ea):
+    assert ea.attn_bwd_workspace_bytes(8, 16, 4096, 128) == 8 * 16 * 4096 * 128 * 4
+    assert ea.attn_bwd_workspace_bytes(1, 1, 100, 64) == 128 * 64 * 4      # rows rounded up to 64
+    assert ea.attn_bwd_workspace_bytes(0, 16, 4096, 128) == 0
+    assert ea.attn_bwd_workspace_bytes(1, 1, 128, 96) == 0                  # unsupported d
+
+
+def _raw(ea):
+    return ea._lib
+
+
+def test_validation_errors_do_not_launch(ea):
+    lib = _raw(ea)
+    p = ctypes.c_void_p(4096)             # aligned, never dereferenced: validation fails first
+    f = ctypes.c_float
+    # unsupported head dimension
+    assert lib.attn_fwd(p, p, p, p, p, 1, 1, 128, 96, 1, f(0.1), None) == -2
+    assert b"head dimension" in lib.attn_last_error()
+    # negative size
+    assert lib.attn_fwd(p, p, p, p, p, -1, 1, 128, 64, 1, f(0.1), None) == -1
+    # non-finite scale
+    assert lib.attn_fwd(p, p, p, p, p, 1, 1, 128, 64, 1, f(float("nan")), None) == -1
+    assert lib.attn_bwd(p, p, p, p, p, p, p, p, p, p, 1 << 30, 1, 1, 128, 64, 1, f(float("inf")), None) == -1
+    # null and misaligned pointers
+    assert lib.attn_fwd(None, p, p, p, p, 1, 1, 128, 64, 1, f(0.1), None) == -1
+    assert b"q is NULL" in lib.attn_last_error()
+    assert lib.attn_fwd(p, ctypes.c_void_p(4098), p, p, p, 1, 1, 128, 64, 1, f(0.1), None) == -1
+    assert b"aligned" in lib.attn_last_error()
+    assert lib.attn_bwd_preprocess(p, p, ctypes.c_void_p(4097), 1, 1, 128, 64, None) == -1
+    # workspace too small
+    need = lib.attn_bwd_workspace_bytes(2, 3, 200, 128)
+    assert lib.attn_bwd(p, p, p, p, p, p, p, p, p, p, need - 1, 2, 3, 200, 128, 0, f(0.1), None) == -4
+    assert b"workspace" in lib.attn_last_error()
+    # sizes too large for the grid
+    assert lib.attn_fwd(p, p, p, p, p, 1 << 20, 1 << 10, 1 << 20, 64, 0, f(0.1), None) == -2
+
+
+def test_empty_problems_are_noops(ea):
+    lib = _raw(ea)
+    f = ctypes.c_float
+    # nothing to do: OK without touching any pointer or the GPU
+    assert lib.attn_fwd(None, None, None, None, None, 0, 4, 128, 64, 1, f(0.1), None) == 0
+    assert lib.attn_fwd(None, None, None, None, None, 2, 4, 0, 128, 0, f(0.1), None) == 0
+    assert lib.attn_bwd_preprocess(None, None, None, 2, 0, 64, 64, None) == 0
+    assert lib.attn_bwd(None, None, None, None, None, None, None, None, None, None, 0, 0, 1, 1, 64, 1, f(0.1), None) == 0
+    assert lib.attn_last_error() == b""
+
+
+def test_version(ea):
+    assert "gfx950" in ea.version()
