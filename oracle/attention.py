@@ -133,13 +133,20 @@ def softmax_backward(p: np.ndarray, dp: np.ndarray, D: np.ndarray) -> np.ndarray
     return p * (dp - D[..., None])
 
 
-def attention_backward(q, k, v, do, scale: float, causal: bool = False, allowed=None):
+def attention_backward(q, k, v, do, scale: float, causal: bool = False, allowed=None,
+                       o_for_D=None):
     """Backward pass.  Returns a dict with dq, dk, dv, D and the recomputed o,
     lse, all float64.
 
     S and P are recomputed from Q and K with a plain softmax; then
     dV = P^T dO, dP = dO V^T, D = rowsum(dO o O), dS = P o (dP - D),
-    dQ = scale * dS K, dK = scale * dS^T Q."""
+    dQ = scale * dS K, dK = scale * dS^T Q.
+
+    ``o_for_D``: the O that the backward is given.  The preprocess of the
+    attention-backward page ("Precomputing D") forms D from the O the forward
+    stored, before the main loop; pass that stored O here (e.g. the forward's O
+    rounded to the storage format) to follow that data flow.  By default D uses
+    the exact O recomputed here."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -154,7 +161,7 @@ def attention_backward(q, k, v, do, scale: float, causal: bool = False, allowed=
     o = p @ v
     dv = np.swapaxes(p, -1, -2) @ do
     dp = do @ np.swapaxes(v, -1, -2)
-    D = bwd_preprocess(o, do)
+    D = bwd_preprocess(o if o_for_D is None else o_for_D, do)
     ds = softmax_backward(p, dp, D)
     del p, dp
     dq = scale * (ds @ k)

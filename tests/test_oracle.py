@@ -251,6 +251,26 @@ def test_backward_identities(causal):
     assert np.allclose((v * g["dv"]).sum((-1, -2)), g["D"].sum(-1), rtol=1e-10, atol=1e-10)
 
 
+def test_stored_o_changes_only_D_path():
+    """D taken from a given O: with the exact O nothing changes; with another O
+    only D, dS, dQ and dK move, and dQ/dK move by exactly -scale*(dD)(P K) /
+    -scale*P^T(dD Q)."""
+    rng = np.random.default_rng(31)
+    n, d, scale = 10, 4, 0.5
+    q, k, v, do = (_rand(rng, 1, 1, n, d) for _ in range(4))
+    g0 = oracle.attention_backward(q, k, v, do, scale, causal=True)
+    g1 = oracle.attention_backward(q, k, v, do, scale, causal=True, o_for_D=g0["o"])
+    for name in ("dq", "dk", "dv", "D"):
+        assert np.array_equal(g0[name], g1[name])
+    o2 = g0["o"] + 0.01 * _rand(rng, 1, 1, n, d)
+    g2 = oracle.attention_backward(q, k, v, do, scale, causal=True, o_for_D=o2)
+    assert np.array_equal(g0["dv"], g2["dv"])
+    dD = np.sum(do * (o2 - g0["o"]), -1)                       # change of D per row
+    p = oracle.softmax_rows(oracle.scores(q, k, scale, oracle.causal_allowed(n, n)))
+    assert np.allclose(g2["dq"] - g0["dq"], -scale * dD[..., None] * (p @ k), atol=1e-13)
+    assert np.allclose(g2["dk"] - g0["dk"], -scale * np.swapaxes(p, -1, -2) @ (dD[..., None] * q), atol=1e-13)
+
+
 def test_empty_sparse_row_gives_zero():
     rng = np.random.default_rng(2)
     q = _rand(rng, 2, 3, 4)
