@@ -5,6 +5,12 @@ Tolerances (per output tensor, bf16 inputs):
   max |gpu - ref|            <= 2e-2 * max |ref|
   sum |gpu - ref| / sum |ref| <= 5e-3            (mean-abs relative error)
   log-sum-exp: max |gpu - ref| <= 1e-3 (absolute)
+A reference that is exactly zero everywhere (dQ, dK when N = 1) is checked
+absolutely: max |gpu| <= 1e-5.
+Adversarial input regimes (wide_logits, late_spike) may pass a `floor`: the
+same metrics of PyTorch's CPU bf16 attention on the same inputs against the
+same oracle; the bound is then max(bar, 1.5 * floor), the noise-floor practice
+of the flash_attention_cuda README's validation.
 """
 import sys
 
@@ -15,6 +21,8 @@ from attn_inputs import bf16_bits_to_f64, f32_to_bf16_bits
 MAX_REL = 2e-2
 MEAN_REL = 5e-3
 LSE_ABS = 1e-3
+ZERO_ABS = 1e-5
+FLOOR_FACTOR = 1.5
 
 
 def say(msg):
@@ -50,14 +58,37 @@ def metrics(gpu: np.ndarray, ref: np.ndarray):
     }
 
 
-def assert_close(name, gpu, ref):
+def assert_close(name, gpu, ref, floor=None):
     assert gpu.shape == ref.shape, (name, gpu.shape, ref.shape)
     assert np.all(np.isfinite(gpu)), f"{name}: non-finite values"
+    if ref.size and float(np.max(np.abs(ref))) == 0.0:
+        mx = float(np.max(np.abs(gpu)))
+        say(f"  {name}: reference is exactly 0, max|gpu|={mx:.3e}")
+        assert mx <= ZERO_ABS, (name, mx)
+        return None
     m = metrics(gpu, ref)
-    say(f"  {name}: max_rel={m['max_rel']:.3e} mean_rel={m['mean_rel']:.3e}")
-    assert m["max_rel"] <= MAX_REL, (name, m)
-    assert m["mean_rel"] <= MEAN_REL, (name, m)
+    max_bar, mean_bar = MAX_REL, MEAN_REL
+    if floor is not None:
+        max_bar = max(max_bar, FLOOR_FACTOR * floor["max_rel"])
+        mean_bar = max(mean_bar, FLOOR_FACTOR * floor["mean_rel"])
+    say(f"  {name}: max_rel={m['max_rel']:.3e} (<= {max_bar:.2e}) mean_rel={m['mean_rel']:.3e} (<= {mean_bar:.2e})")
+    assert m["max_rel"] <= max_bar, (name, m)
+    assert m["mean_rel"] <= mean_bar, (name, m)
     return m
+
+
+def torch_bf16_floor(q, k, v, do, scale, causal, ref):
+    """Metrics of PyTorch's CPU bf16 attention (forward + autograd backward) on
+    the same bf16 inputs against the oracle results `ref` (dict of float64)."""
+    import torch
+    import torch.nn.functional as F
+    t = lambda x: torch.tensor(x, dtype=torch.float32).to(torch.bfloat16).requires_grad_(True)  # noqa: E731
+    tq, tk, tv = t(q), t(k), t(v)
+    o = F.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=scale)
+    o.backward(torch.tensor(do, dtype=torch.float32).to(torch.bfloat16))
+    got = {"o": o.detach().double().numpy(), "dq": tq.grad.double().numpy(),
+           "dk": tk.grad.double().numpy(), "dv": tv.grad.double().numpy()}
+    return {n: metrics(got[n], ref[n]) for n in got}
 
 
 def assert_lse(gpu, ref):

@@ -18,7 +18,7 @@ import pytest
 
 import oracle
 from attn_inputs import DENSE_CONFIGS, DenseConfig, bf16_bits_to_f64, f32_to_bf16_bits, make_dense_inputs
-from _util import assert_close, assert_lse, f64_to_dev_bf16, from_dev, say, to_dev
+from _util import assert_close, assert_lse, f64_to_dev_bf16, from_dev, say, to_dev, torch_bf16_floor
 
 pytestmark = pytest.mark.gpu
 
@@ -62,12 +62,12 @@ def _oracle_heads(inp, cfg, heads, stored_o=False):
     return {n: np.stack(v) for n, v in res.items()}
 
 
-def _compare(out, ref, cfg, heads):
+def _compare(out, ref, cfg, heads, floor=None):
     BH = cfg.B * cfg.H
     for n in ("o", "D", "dq", "dk", "dv"):
         gpu = from_dev(out[n])
         gpu = gpu.reshape((BH,) + gpu.shape[2:])[heads]
-        assert_close(n, gpu, ref[n])
+        assert_close(n, gpu, ref[n], floor=None if floor is None else floor.get(n))
     lse = from_dev(out["lse"]).reshape(BH, cfg.N)[heads]
     assert_lse(lse, ref["lse"])
 
@@ -96,12 +96,20 @@ def test_small_end_to_end(lib, name, regime):
     inp = make_dense_inputs(cfg, regime)
     out = _gpu_path(lib, inp, cfg)
     heads = list(range(cfg.B * cfg.H))
-    # The workloads themselves (gaussian inputs) are held to the bar against the
-    # exact definition.  In the adversarial regimes softmax rows are nearly
-    # one-hot, so dS = P (dP - D) cancels at the peak and the bf16 storage of O
-    # that the method's preprocess reads dominates: there the reference forms
-    # D from the oracle's O stored in bf16, as the method does.
-    _compare(out, _oracle_heads(inp, cfg, heads, stored_o=(regime != "gaussian")), cfg, heads)
+    ref = _oracle_heads(inp, cfg, heads)
+    floor = None
+    if regime != "gaussian":
+        # The workloads themselves (gaussian inputs) are held to the plain bar.
+        # In the adversarial regimes dS = P (dP - D) cancels (near one-hot rows)
+        # or the spiked keys share a large common part that cancels in dS K, so
+        # the bf16 operands the method prescribes (stored O, P and dS) set an
+        # error floor that sits near the bar; there the bound also admits 1.5x
+        # the error of PyTorch's CPU bf16 attention on the same inputs.
+        f = {n: bf16_bits_to_f64(inp[n]) for n in ("q", "k", "v", "do")}
+        full = {n: ref[n].reshape((cfg.B, cfg.H) + ref[n].shape[1:]) for n in ("o", "dq", "dk", "dv")}
+        floor = torch_bf16_floor(f["q"], f["k"], f["v"], f["do"], cfg.scale, cfg.causal, full)
+        say("  floor (torch cpu bf16): " + ", ".join(f"{n} {m['mean_rel']:.2e}" for n, m in floor.items()))
+    _compare(out, ref, cfg, heads, floor=floor)
 
 
 @pytest.mark.parametrize("cfg", RAGGED, ids=lambda c: c.name)
