@@ -27,6 +27,8 @@
 //    workgroup barriers of an iteration.
 //  * P = exp(scale * S - L) is evaluated as 2^(S * scale * log2 e - L * log2 e)
 //    with v_exp_f32.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -59,37 +61,22 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(
     }
 }
 
-// Zero an fp32 buffer of n4 float4 entries (the dQ workspace).
-__global__ __launch_bounds__(256) void fill_zero_kernel(f32x4* __restrict__ p, long long n4) {
-    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n4;
-         i += (long long)gridDim.x * 256)
-        p[i] = z;
-}
-
-// dQ = bf16(scale * dQ_accum) for rows < N of every (batch, head).
-template <int HD>
-__global__ __launch_bounds__(256) void dq_convert_kernel(
-    const float* __restrict__ acc, __bf16* __restrict__ dQ, int BH, int N, int n_pad,
-    float scale) {
-    constexpr int CPR = HD / 8;                 // 8-element chunks per row
-    const long long total = (long long)BH * N * CPR;
-    for (long long c = (long long)blockIdx.x * 256 + threadIdx.x; c < total;
-         c += (long long)gridDim.x * 256) {
-        const long long row = c / CPR;          // bh * N + n
-        const int part = (int)(c % CPR);
-        const long long bh = row / N;
-        const long long n = row % N;
-        const float* src = acc + ((size_t)(bh * n_pad + n) * HD + part * 8);
-        const f32x4 a = *reinterpret_cast<const f32x4*>(src);
-        const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
-        f32x8 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            v[e] = a[e] * scale;
-            v[e + 4] = b[e] * scale;
-        }
-        *reinterpret_cast<bf16x8*>(dQ + (size_t)row * HD + part * 8) = to_bf16x8(v);
+// Backward prep: the per-row statistics the dK/dV kernel copies into LDS,
+// padded to the 64-row query tile: Lb = L * log2(e) (+inf past the end, so
+// P = 2^-inf = 0 there) and D (0 past the end).
+__global__ __launch_bounds__(256) void bwd_prep_kernel(float* __restrict__ Lb,
+                                                       float* __restrict__ Dp,
+                                                       const float* __restrict__ lse,
+                                                       const float* __restrict__ D, int BH, int N,
+                                                       int n_pad) {
+    const long long rows = (long long)BH * n_pad;
+    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < rows;
+         i += (long long)gridDim.x * 256) {
+        const long long bh = i / n_pad;
+        const int n = (int)(i % n_pad);
+        const bool in = n < N;
+        Lb[i] = in ? lse[bh * N + n] * kLog2e : __builtin_inff();
+        Dp[i] = in ? D[bh * N + n] : 0.f;
     }
 }
 
@@ -98,123 +85,155 @@ __global__ __launch_bounds__(256) void dq_convert_kernel(
 // ----------------------------------------------------------------------------
 namespace bwd {
 
-constexpr int BC = 128;          // keys per workgroup (4 waves x 32)
-constexpr int BR = 64;           // query rows per iteration (2 blocks of 32)
-constexpr int NT = 256;          // threads
+constexpr int BC = 128;          // keys per workgroup
+constexpr int BR = 64;           // query rows per iteration
+constexpr int NW = 8;            // wave64s per workgroup (2 per SIMD)
+constexpr int NT = NW * 64;
 
-// Row-major tiles in LDS are padded by 16 bytes per row so that the 16-byte
-// operand reads of eight consecutive rows fall on distinct banks.
+// LDS tiles (all unpadded):
+//  * row-major [rows][HD] tiles (Q_i, dO_i, K_j, V_j): the 16-byte chunk c of
+//    row r lives at chunk c ^ rswz(r).  rswz takes the 8 values 0,2,4,6,1,3,5,7
+//    on any 8 consecutive rows, so the 16-byte operand reads of 8 consecutive
+//    rows hit 8 distinct bank groups, and on 4 consecutive rows it separates
+//    the two chunks a transposing read takes from each row.
+//  * dS^T [BC keys][BR queries] (workspace tiles, copied unchanged into the
+//    dQ kernel's LDS): the 8-byte unit u of row `key` lives at unit
+//    u ^ tswz(key), a bit permutation of the low 4 key bits, so 16 consecutive
+//    keys written at the same unit, and 4 keys x 4 units read by one
+//    transposing read, are all on distinct banks.
+__device__ __forceinline__ int rswz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
+template <int HD>
+__device__ __forceinline__ int roff(int r, int c) {      // chunk c of row r (elements)
+    return r * HD + ((c ^ rswz(r)) << 3);
+}
+
+template <int HD>
+__device__ __forceinline__ int roff4(int r, int col) {   // 4 elements at col (multiple of 4)
+    return r * HD + ((((col >> 3) ^ rswz(r))) << 3) + (col & 4);
+}
+
+__device__ __forceinline__ int tswz(int key) { return ((key & 3) << 2) | ((key >> 2) & 3); }
+
+__device__ __forceinline__ int toff(int key, int u) {     // unit u (4 queries) of row key
+    return key * BR + ((u ^ tswz(key)) << 2);
+}
+
 template <int HD> struct Smem {
-    static constexpr int QS = HD + 8;            // Q / dO row stride (elements)
-    static constexpr int SS = BC + 8;            // dS row stride
-    static constexpr int KTS = BC + 8;           // K^T staging row stride
-    // transposed Q^T / dO^T: HD rows of BR = 64 queries = 16 chunks of 8 bytes,
-    // unpadded, chunk index XOR-swizzled by the row.
-    static constexpr int TS = BR;
-    static constexpr int off_q = 0;
-    static constexpr int off_do = off_q + BR * QS * 2;
-    static constexpr int off_qt = off_do + BR * QS * 2;
-    static constexpr int off_dot = off_qt + HD * TS * 2;
-    static constexpr int off_ds = off_dot + HD * TS * 2;
-    static constexpr int off_l = off_ds + BR * SS * 2;
-    static constexpr int off_d = off_l + BR * 4;
-    static constexpr int bytes = off_d + BR * 4;
-    // K^T staging (prologue only) overlays the Q and dO tiles.
-    static constexpr int off_kt = 0;
-    static_assert(HD * KTS * 2 <= off_qt, "K^T staging must fit in the Q/dO area");
+    static constexpr int TILE = BR * HD * 2;              // one Q_i or dO_i tile (bytes)
+    static constexpr int off_q = 0;                       // two buffers
+    static constexpr int off_do = 2 * TILE;               // two buffers
+    static constexpr int off_k = 4 * TILE;
+    static constexpr int off_v = off_k + BC * HD * 2;
+    static constexpr int off_l = off_v + BC * HD * 2;     // float[2][BR]
+    static constexpr int off_d = off_l + 2 * BR * 4;      // float[2][BR]
+    static constexpr int bytes = off_d + 2 * BR * 4;
+    // the dK / dV partial exchange of the epilogue overlays [0, off_l)
+    static constexpr int xchg = 4 * 2 * (HD / 32) * 16 * 64 * 4;
+    static_assert(xchg <= off_l, "partial exchange must fit below L / D");
 };
 
-// Swizzled position (in elements) of 8-byte chunk `ch` (0..15) of row `r` of a
-// transposed tile with 64 elements per row.  The XOR keeps both the operand
-// reads (16 consecutive rows, same chunk) and the staging writes (rows 8
-// apart, same chunk) on distinct banks.
-__device__ __forceinline__ int tswz(int r, int ch) {
-    return r * BR + (((ch ^ (r ^ (r >> 4))) & 15) << 2);
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane i receives element i % 4 of the 8 bytes addressed by lanes i / 4,
+// 4 + i / 4, 8 + i / 4 and 12 + i / 4.  If lane t of the group addresses row
+// r0 + t / 4, columns c0 + 4 (t % 4) .. + 3 of a row-major tile, lane i gets
+// column c0 + i of rows r0 .. r0 + 3.
+__device__ __forceinline__ bf16x4 lds_read_tr(const __bf16* p) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(p));
+    return __builtin_bit_cast(bf16x4, v);
 }
 
-// Per-thread share of one Q (or dO) tile: 4 consecutive rows x 8 columns.
-template <int HD> struct TileRegs {
-    u32x4 q[4], g[4];
-    float l, d;
-};
-
-template <int HD>
-__device__ __forceinline__ void load_tile(TileRegs<HD>& tr, const __bf16* Qh, const __bf16* dOh,
-                                          const float* Lh, const float* Dh, int q0, int N) {
-    constexpr int CG = HD / 8;                   // column groups
-    const int t = threadIdx.x;
-    if (t < 16 * CG) {
-        const int cg = t % CG, rg = t / CG;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = q0 + rg * 4 + r;
-            if (row < N) {
-                tr.q[r] = gload16(Qh + (size_t)row * HD + cg * 8);
-                tr.g[r] = gload16(dOh + (size_t)row * HD + cg * 8);
-            } else {
-                tr.q[r] = u32x4{0u, 0u, 0u, 0u};
-                tr.g[r] = u32x4{0u, 0u, 0u, 0u};
-            }
-        }
-    }
-    if (t < BR) {
-        const int row = q0 + t;
-        // rows past the end get L = +inf, so P = 2^-inf = 0 there
-        tr.l = row < N ? Lh[row] * kLog2e : __builtin_inff();
-        tr.d = row < N ? Dh[row] : 0.f;
-    }
+// Direct global -> LDS copy: lane l of the wave writes its `bytes` (4 or 16)
+// at lds_base + l * bytes; lds_base is the same for the whole wave.
+__device__ __forceinline__ void dma16(const void* src, void* lds_base) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
 }
 
-template <int HD>
-__device__ __forceinline__ void store_tile(const TileRegs<HD>& tr, char* smem) {
-    using S = Smem<HD>;
-    constexpr int CG = HD / 8;
-    const int t = threadIdx.x;
-    __bf16* Qs = reinterpret_cast<__bf16*>(smem + S::off_q);
-    __bf16* dOs = reinterpret_cast<__bf16*>(smem + S::off_do);
-    __bf16* QT = reinterpret_cast<__bf16*>(smem + S::off_qt);
-    __bf16* dOT = reinterpret_cast<__bf16*>(smem + S::off_dot);
-    if (t < 16 * CG) {
-        const int cg = t % CG, rg = t / CG;
+__device__ __forceinline__ void dma4(const void* src, void* lds_base) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 4, 0, 0);
+}
+
+// Copy rows [row0, row0 + ROWS) of a [*, HD] bf16 tensor into a swizzled LDS
+// tile with WAVES waves; rows at or past N re-read row N - 1 (finite values
+// whose contributions are masked to zero).
+template <int HD, int ROWS, int WAVES>
+__device__ __forceinline__ void stage_rows(const __bf16* src, int row0, int N, char* tile, int w,
+                                           int lane) {
+    constexpr int CPR = HD / 8;
+    constexpr int IPW = ROWS * CPR / 64 / WAVES;          // instructions per wave
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            *reinterpret_cast<u32x4*>(Qs + (rg * 4 + r) * S::QS + cg * 8) = tr.q[r];
-            *reinterpret_cast<u32x4*>(dOs + (rg * 4 + r) * S::QS + cg * 8) = tr.g[r];
-        }
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const int drow = cg * 8 + c;
-            *reinterpret_cast<u32x2*>(QT + tswz(drow, rg)) =
-                column4(tr.q[0], tr.q[1], tr.q[2], tr.q[3], c);
-            *reinterpret_cast<u32x2*>(dOT + tswz(drow, rg)) =
-                column4(tr.g[0], tr.g[1], tr.g[2], tr.g[3], c);
-        }
-    }
-    if (t < BR) {
-        reinterpret_cast<float*>(smem + S::off_l)[t] = tr.l;
-        reinterpret_cast<float*>(smem + S::off_d)[t] = tr.d;
+    for (int i = 0; i < IPW; ++i) {
+        const int I = w * IPW + i;
+        const int P = I * 64 + lane;                       // physical chunk
+        const int r = P / CPR;
+        const int c = (P % CPR) ^ rswz(r);                 // logical chunk stored there
+        const int row = min(row0 + r, N - 1);
+        dma16(src + (size_t)row * HD + c * 8, tile + I * 1024);
     }
 }
 
+// Copy BYTES contiguous bytes (a multiple of WAVES * 1024) into LDS.
+template <int BYTES, int WAVES>
+__device__ __forceinline__ void stage_bytes(const char* src, char* dst, int w, int lane) {
+    constexpr int IPW = BYTES / 1024 / WAVES;
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+        const int I = w * IPW + i;
+        dma16(src + I * 1024 + lane * 16, dst + I * 1024);
+    }
+}
+
+// Workspace tile of dS^T for one (batch*head, query tile i, key tile j):
+// BC x BR bf16 in the swizzled dS^T layout (toff), so the dQ kernel can copy it
+// into LDS unchanged.
+constexpr int DST_EL = BC * BR;
+
+__device__ __forceinline__ size_t dst_tile(int bh, int i, int j, int tr, int tc) {
+    return ((size_t)((size_t)bh * tr + i) * tc + j) * DST_EL;
+}
+
+// ----------------------------------------------------------------------------
+// Kernel A: one workgroup per (batch*head, 128-key tile j).  Walks the query
+// tiles i (from the diagonal tile when causal), recomputes S_ij and P_ij from
+// L, forms dP_ij and dS_ij, accumulates dV_j = sum P^T dO and dK_j = sum dS^T Q
+// in registers, and stores dS_ij^T (bf16) for the dQ kernel.
+//
+// Eight wave64s (two per SIMD): wave (kw, qh) owns keys 32 kw .. + 31 and query
+// rows 32 qh .. + 31 of each 64-row tile; the two waves that share keys add
+// their dK / dV partials through LDS at the end.  Q_i / dO_i are double
+// buffered in LDS by direct global -> LDS copies issued one tile ahead; K_j and
+// V_j stay in LDS.  The accumulator layout of S / dP (one key per lane) is the A
+// layout of P^T and dS^T, so dV and dK take P and dS straight from registers
+// with the query index relabelled consistently on the B side, whose operands
+// (dO, Q with one head-dim column per lane) come from transposing LDS reads.
+// ----------------------------------------------------------------------------
 template <int HD, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1)))
-void bwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+__global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2, 2)))
+void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                      const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
-                     const float* __restrict__ Lse, const float* __restrict__ Dd,
-                     float* __restrict__ dQacc, __bf16* __restrict__ dK,
+                     const float* __restrict__ Lb, const float* __restrict__ Dp,
+                     __bf16* __restrict__ dSw, __bf16* __restrict__ dK,
                      __bf16* __restrict__ dV, int BH, int N, int n_pad, float scale) {
     using S = Smem<HD>;
     constexpr int KSD = HD / 16;                 // k steps over the head dim
     constexpr int DB = HD / 32;                  // 32-wide blocks of the head dim
-    constexpr int DQT = 2 * DB / 4;              // dQ output tiles per wave
+    constexpr int TILE_EL = BR * HD;             // elements of one Q_i / dO_i buffer
     extern __shared__ __attribute__((aligned(16))) char smem[];
 
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
+    const int kw = w & 3;                        // this wave's 32 keys of the 128
+    const int qh = w >> 2;                       // this wave's 32 query rows of the 64
     const int l32 = lane & 31;
     const int g = lane >> 5;
+    const int t16 = lane & 15;                   // lane within its 16-lane group
+    const int hh = (lane >> 4) & 1;              // which 16-lane half of the 32
+    const int s4 = t16 >> 2;                     // row offset inside a transposing read
 
     const int tc = (N + BC - 1) / BC;
+    const int tr_count = (N + BR - 1) / BR;
     const int logical = xcd_remap(blockIdx.x, BH * tc);
     const int bh = logical / tc;
     const int j = logical % tc;                  // heavy (small j) first when causal
@@ -222,55 +241,58 @@ void bwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 
     const size_t head = (size_t)bh * N * HD;
     const __bf16* Qh = Q + head;
-    const __bf16* Kh = K + head;
-    const __bf16* Vh = V + head;
     const __bf16* dOh = dO + head;
-    const float* Lh = Lse + (size_t)bh * N;
-    const float* Dh = Dd + (size_t)bh * N;
-    float* dQh = dQacc + (size_t)bh * n_pad * HD;
+    const float* Lbh = Lb + (size_t)bh * n_pad;
+    const float* Dph = Dp + (size_t)bh * n_pad;
 
-    // ---- K, V as B operands of S = Q K^T and dP = dO V^T (this wave's 32 keys)
-    bf16x8 kb[KSD], vb[KSD];
+    __bf16* const QB = reinterpret_cast<__bf16*>(smem + S::off_q);   // Q buffers; dO at +2 tiles
+    __bf16* const KB = reinterpret_cast<__bf16*>(smem + S::off_k);   // K; V at +BC*HD
+    float* const LB = reinterpret_cast<float*>(smem + S::off_l);     // L buffers; D at +2*BR
+
+    // ---- loop-invariant per-lane LDS offsets (elements); every access below
+    //      is one of these plus a compile-time constant
+    // row reads of the A / B operands of S and dP: chunk 2ks+g of row rq / rk;
+    // k steps ks and ks + 4 differ by 8 chunks, which the swizzle leaves alone
+    int oq[4], okr[4];
     {
-        const int key = k0 + w * 32 + l32;
+        const int rq = qh * 32 + l32, rk = kw * 32 + l32;
 #pragma unroll
-        for (int ks = 0; ks < KSD; ++ks) {
-            if (key < N) {
-                kb[ks] = __builtin_bit_cast(bf16x8, gload16(Kh + (size_t)key * HD + ks * 16 + g * 8));
-                vb[ks] = __builtin_bit_cast(bf16x8, gload16(Vh + (size_t)key * HD + ks * 16 + g * 8));
-            } else {
-                kb[ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-                vb[ks] = kb[ks];
-            }
+        for (int i = 0; i < 4; ++i) {
+            oq[i] = roff<HD>(rq, 2 * i + g);
+            okr[i] = roff<HD>(rk, 2 * i + g);
         }
     }
-
-    // ---- K^T as the B operand of dQ = dS K: staged transposed through LDS once
-    const int dq_db = (DB == 4) ? w : (w & 1);   // this wave's 32 head-dim columns of dQ
-    const int dq_qb0 = (DB == 4) ? 0 : (w >> 1); // first query block it covers
-    bf16x8 kt[BC / 16];
+    // transposing reads of dO_i / Q_i (B operands of dV, dK): rows
+    // qh*32 + 16 k4 + 4g + s4 (+8), columns 32 db + 16 hh + 4 (t16 & 3); the
+    // row swizzle is the same for every k4 and for +8, and head-dim blocks
+    // 2, 3 sit 8 chunks after blocks 0, 1
+    int otr[2];
     {
-        __bf16* KT = reinterpret_cast<__bf16*>(smem + S::off_kt);
-        constexpr int CG = HD / 8;
-        for (int blk = threadIdx.x; blk < (BC / 4) * CG; blk += NT) {
-            const int cg = blk % CG, rg = blk / CG;
-            u32x4 r4[4];
+        const int ra = qh * 32 + g * 4 + s4;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int key = k0 + rg * 4 + r;
-                r4[r] = key < N ? gload16(Kh + (size_t)key * HD + cg * 8) : u32x4{0u, 0u, 0u, 0u};
-            }
-#pragma unroll
-            for (int c = 0; c < 8; ++c)
-                *reinterpret_cast<u32x2*>(KT + (cg * 8 + c) * S::KTS + rg * 4) =
-                    column4(r4[0], r4[1], r4[2], r4[3], c);
-        }
-        __syncthreads();
-#pragma unroll
-        for (int ks = 0; ks < BC / 16; ++ks)
-            kt[ks] = lds_read16(KT + (dq_db * 32 + l32) * S::KTS + ks * 16 + g * 8);
-        __syncthreads();
+        for (int db = 0; db < 2; ++db)
+            otr[db] = roff4<HD>(ra, db * 32 + hh * 16 + 4 * (t16 & 3));
     }
+    // dS^T stores: this lane's key, units qh*8 + 2 rr + g of the workspace tile
+    int ow[4];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) ow[rr] = toff(kw * 32 + l32, qh * 8 + rr * 2 + g);
+    const int ol = qh * 32 + g * 4;              // L / D rows of this lane (+ 8 rr)
+
+    const int it0 = CAUSAL ? (k0 / BR) : 0;
+
+    // ---- K_j, V_j and the first Q_i / dO_i tile (with its L, D rows) to LDS
+    auto stage_tile = [&](int it, int buf) {
+        const int q0 = it * BR;
+        stage_rows<HD, BR, NW>(Qh, q0, N, smem + S::off_q + buf * S::TILE, w, lane);
+        stage_rows<HD, BR, NW>(dOh, q0, N, smem + S::off_do + buf * S::TILE, w, lane);
+        if (w == 0) dma4(Lbh + q0 + lane, smem + S::off_l + buf * BR * 4);
+        if (w == 1) dma4(Dph + q0 + lane, smem + S::off_d + buf * BR * 4);
+    };
+    stage_rows<HD, BC, NW>(K + head, k0, N, smem + S::off_k, w, lane);
+    stage_rows<HD, BC, NW>(V + head, k0, N, smem + S::off_v, w, lane);
+    stage_tile(it0, 0);
+    __syncthreads();
 
     f32x16 dv[DB], dk[DB];
 #pragma unroll
@@ -279,138 +301,195 @@ void bwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         dk[b] = zero16();
     }
 
-    const int tr_count = (N + BR - 1) / BR;
-    const int it0 = CAUSAL ? (k0 / BR) : 0;
-
-    const __bf16* Qs = reinterpret_cast<const __bf16*>(smem + S::off_q);
-    const __bf16* dOs = reinterpret_cast<const __bf16*>(smem + S::off_do);
-    const __bf16* QT = reinterpret_cast<const __bf16*>(smem + S::off_qt);
-    const __bf16* dOT = reinterpret_cast<const __bf16*>(smem + S::off_dot);
-    __bf16* dSs = reinterpret_cast<__bf16*>(smem + S::off_ds);
-    const float* Ls = reinterpret_cast<const float*>(smem + S::off_l);
-    const float* Ds = reinterpret_cast<const float*>(smem + S::off_d);
-
-    TileRegs<HD> pre;
-    load_tile<HD>(pre, Qh, dOh, Lh, Dh, it0 * BR, N);
-    store_tile<HD>(pre, smem);
-    __syncthreads();
-
     const float sl2 = scale * kLog2e;
-    const int key_lane = k0 + w * 32 + l32;      // this lane's key (accumulator column)
+    const int key_lane = k0 + kw * 32 + l32;     // this lane's key (accumulator column)
 
-    for (int it = it0; it < tr_count; ++it) {
+    auto iteration = [&](int it, auto bufc) {
+        constexpr int BUF = decltype(bufc)::value;
+        const __bf16* Qs = QB + BUF * TILE_EL;
+        const __bf16* dOs = QB + (2 + BUF) * TILE_EL;
+        const float* Ls = LB + BUF * BR;
+        const float* Ds = LB + (2 + BUF) * BR;
         const int q0 = it * BR;
-        const bool has_next = it + 1 < tr_count;
-        if (has_next) load_tile<HD>(pre, Qh, dOh, Lh, Dh, q0 + BR, N);
+        if (it + 1 < tr_count) stage_tile(it + 1, BUF ^ 1);     // lands during this iteration
 
-        // ---- S = Q K^T and dP = dO V^T for 64 queries x this wave's 32 keys
-        f32x16 s[2], dp[2];
-        s[0] = zero16(); s[1] = zero16(); dp[0] = zero16(); dp[1] = zero16();
+        // ---- S = Q K^T, dP = dO V^T: this wave's 32 queries x 32 keys
+        f32x16 s = zero16(), dp = zero16();
 #pragma unroll
         for (int ks = 0; ks < KSD; ++ks) {
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                const bf16x8 a = lds_read16(Qs + (qb * 32 + l32) * S::QS + ks * 16 + g * 8);
-                const bf16x8 b = lds_read16(dOs + (qb * 32 + l32) * S::QS + ks * 16 + g * 8);
-                s[qb] = mfma32(a, kb[ks], s[qb]);
-                dp[qb] = mfma32(b, vb[ks], dp[qb]);
-            }
+            const int hi = (ks >> 2) * 64;
+            s = mfma32(lds_read16(Qs + oq[ks & 3] + hi), lds_read16(KB + okr[ks & 3] + hi), s);
+            dp = mfma32(lds_read16(dOs + oq[ks & 3] + hi),
+                        lds_read16(KB + BC * HD + okr[ks & 3] + hi), dp);
         }
 
         // ---- P = exp(scale*S - L), dS = P o (dP - D); masked entries give 0
-        const bool need_mask = (k0 + BC > N) || (CAUSAL && (k0 + BC - 1 > q0));
+        const bool need_mask = (k0 + BC > N) || (CAUSAL && (k0 + kw * 32 + 31 > q0 + qh * 32));
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+        for (int rr = 0; rr < 4; ++rr) {
+            const f32x4 lv = *reinterpret_cast<const f32x4*>(Ls + ol + rr * 8);
+            const f32x4 dd = *reinterpret_cast<const f32x4*>(Ds + ol + rr * 8);
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int qrow = qb * 32 + rr * 8 + g * 4;          // 4 consecutive rows
-                const f32x4 lv = *reinterpret_cast<const f32x4*>(Ls + qrow);
-                const f32x4 dd = *reinterpret_cast<const f32x4*>(Ds + qrow);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = rr * 4 + e;
-                    float x = s[qb][r] * sl2 - lv[e];
-                    if (need_mask) {
-                        const int qg = q0 + qrow + e;
-                        const bool masked = (key_lane >= N) || (CAUSAL && key_lane > qg);
-                        x = masked ? -__builtin_inff() : x;
-                    }
-                    const float p = __builtin_amdgcn_exp2f(x);
-                    s[qb][r] = p;
-                    dp[qb][r] = p * (dp[qb][r] - dd[e]);
+            for (int e = 0; e < 4; ++e) {
+                const int r = rr * 4 + e;
+                float x = __builtin_fmaf(s[r], sl2, -lv[e]);
+                if (need_mask) {
+                    const bool masked = (key_lane >= N) ||
+                                        (CAUSAL && key_lane > q0 + ol + rr * 8 + e);
+                    x = masked ? -__builtin_inff() : x;
                 }
+                const float p = __builtin_amdgcn_exp2f(x);
+                s[r] = p;
+                dp[r] = p * (dp[r] - dd[e]);
             }
         }
+        // ---- P^T, dS^T as A operands (k = query, relabelled per lane group)
+        const bf16x8 pa0 = pack_c8(s, 0), pa1 = pack_c8(s, 8);
+        const bf16x8 ds0 = pack_c8(dp, 0), ds1 = pack_c8(dp, 8);
 
-        // ---- P^T and dS^T as A operands (k = query, relabelled per lane group)
-        bf16x8 pa[4], dsa[4];
-#pragma unroll
-        for (int k4 = 0; k4 < 4; ++k4) {
-            pa[k4] = pack_c8(s[k4 >> 1], (k4 & 1) * 8);
-            dsa[k4] = pack_c8(dp[k4 >> 1], (k4 & 1) * 8);
-        }
-
-        // ---- dS to LDS, one query per row, for dQ = dS K
-#pragma unroll
-        for (int k4 = 0; k4 < 4; ++k4) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int r = (k4 & 1) * 8 + e;
-                const int qrow = (k4 >> 1) * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-                dSs[qrow * S::SS + w * 32 + l32] = dsa[k4][e];
-            }
-        }
-
-        // ---- dV += P^T dO, dK += dS^T Q (B operands from the transposed tiles)
+        // ---- dV += P^T dO, dK += dS^T Q over this wave's 32 queries; the B
+        //      operands are read transposed from the row-major dO_i, Q_i tiles
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-            const int drow = db * 32 + l32;
+            const int o = otr[db & 1] + (db >> 1) * 64;
 #pragma unroll
-            for (int k4 = 0; k4 < 4; ++k4) {
-                const bf16x8 bo = cat44(lds_read8(dOT + tswz(drow, 4 * k4 + g)),
-                                        lds_read8(dOT + tswz(drow, 4 * k4 + 2 + g)));
-                const bf16x8 bq = cat44(lds_read8(QT + tswz(drow, 4 * k4 + g)),
-                                        lds_read8(QT + tswz(drow, 4 * k4 + 2 + g)));
-                dv[db] = mfma32(pa[k4], bo, dv[db]);
-                dk[db] = mfma32(dsa[k4], bq, dk[db]);
+            for (int k4 = 0; k4 < 2; ++k4) {
+                const int rk = k4 * 16 * HD;
+                const bf16x8 bo = cat44(lds_read_tr(dOs + o + rk), lds_read_tr(dOs + o + rk + 8 * HD));
+                const bf16x8 bq = cat44(lds_read_tr(Qs + o + rk), lds_read_tr(Qs + o + rk + 8 * HD));
+                dv[db] = mfma32(k4 ? pa1 : pa0, bo, dv[db]);
+                dk[db] = mfma32(k4 ? ds1 : ds0, bq, dk[db]);
             }
         }
+        // the next tile has landed and every read of this tile is done; the dS^T
+        // stores go after the barrier so that its wait for the tile copies does
+        // not also wait for them
+        __syncthreads();
+        __bf16* dst = dSw + dst_tile(bh, it, j, tr_count, tc);
+        *reinterpret_cast<bf16x4*>(dst + ow[0]) = __builtin_shufflevector(ds0, ds0, 0, 1, 2, 3);
+        *reinterpret_cast<bf16x4*>(dst + ow[1]) = __builtin_shufflevector(ds0, ds0, 4, 5, 6, 7);
+        *reinterpret_cast<bf16x4*>(dst + ow[2]) = __builtin_shufflevector(ds1, ds1, 0, 1, 2, 3);
+        *reinterpret_cast<bf16x4*>(dst + ow[3]) = __builtin_shufflevector(ds1, ds1, 4, 5, 6, 7);
+    };
 
-        __syncthreads();                        // dS complete; Q/dO tiles free
-        if (has_next) store_tile<HD>(pre, smem);
-
-        // ---- dQ_i partial = dS K over this workgroup's 128 keys, added atomically
-#pragma unroll
-        for (int tq = 0; tq < DQT; ++tq) {
-            const int qb = dq_qb0 + tq;
-            f32x16 acc = zero16();
-#pragma unroll
-            for (int ks = 0; ks < BC / 16; ++ks) {
-                const bf16x8 a = lds_read16(dSs + (qb * 32 + l32) * S::SS + ks * 16 + g * 8);
-                acc = mfma32(a, kt[ks], acc);
-            }
-            float* dst = dQh + (size_t)(q0 + qb * 32) * HD + dq_db * 32 + l32;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = (r >> 2) * 8 + g * 4 + (r & 3);
-                unsafeAtomicAdd(dst + (size_t)row * HD, acc[r]);
-            }
-        }
-        __syncthreads();                        // next tile visible; dS reads done
+    for (int it = it0; it < tr_count; it += 2) {
+        iteration(it, std::integral_constant<int, 0>());
+        if (it + 1 < tr_count) iteration(it + 1, std::integral_constant<int, 1>());
     }
 
-    // ---- epilogue: dK = scale * sum dS^T Q, dV = sum P^T dO, bf16 (RNE) stores
+    // ---- epilogue: the two waves sharing 32 keys (qh = 0, 1) add their partial
+    //      dK / dV through LDS; qh = 0 stores dV, qh = 1 stores dK (scaled)
+    float* X = reinterpret_cast<float*>(smem);
+    constexpr int PART = DB * 16 * 64;           // floats of one wave's dK (or dV)
+    float* mine = X + (kw * 2 + qh) * PART;      // qh 0 publishes dK, qh 1 publishes dV
+    float* other = X + (kw * 2 + (qh ^ 1)) * PART;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            mine[(db * 16 + r) * 64 + lane] = qh ? dv[db][r] : dk[db][r];
+    __syncthreads();
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int key = k0 + w * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
+            const float tot = (qh ? dk[db][r] : dv[db][r]) + other[(db * 16 + r) * 64 + lane];
+            const int key = k0 + kw * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
             if (key < N) {
                 const size_t off = head + (size_t)key * HD + db * 32 + l32;
-                dK[off] = (__bf16)(dk[db][r] * scale);
-                dV[off] = (__bf16)dv[db][r];
+                if (qh) dK[off] = (__bf16)(tot * scale);
+                else dV[off] = (__bf16)tot;
             }
         }
+    }
+}
+
+// ----------------------------------------------------------------------------
+// Kernel B: dQ_i = scale * sum_j dS_ij K_j, one workgroup per (batch*head,
+// 64-row query tile i).  The dS^T tiles written by kernel A and the K_j tiles
+// are copied into LDS one tile ahead; each wave owns one 32 x 32 block of dQ_i
+// and accumulates it over all key tiles in registers, reading both operands
+// transposed.  No atomics: the reduction over key tiles happens in registers.
+// ----------------------------------------------------------------------------
+template <int HD> struct SmemQ {
+    static constexpr int DS_B = DST_EL * 2;               // one dS^T tile (bytes)
+    static constexpr int K_B = BC * HD * 2;               // one K tile (bytes)
+    static constexpr int off_ds = 0;                      // two buffers
+    static constexpr int off_k = 2 * DS_B;                // two buffers
+    static constexpr int bytes = off_k + 2 * K_B;
+};
+
+template <int HD, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(HD / 16 * 64, HD / 16 * 64)))
+void bwd_dq_kernel(const __bf16* __restrict__ K, const __bf16* __restrict__ dSw,
+                   __bf16* __restrict__ dQ, int BH, int N, float scale) {
+    using S = SmemQ<HD>;
+    constexpr int DB = HD / 32;
+    constexpr int WAVES = 2 * DB;                // one 32 x 32 dQ block per wave
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int qb = w / DB;                       // query block (32 rows) of the tile
+    const int db = w % DB;                       // head-dim block (32 columns)
+    const int l32 = lane & 31;
+    const int g = lane >> 5;
+    const int t16 = lane & 15;
+    const int hh = (lane >> 4) & 1;
+    const int s4 = t16 >> 2;
+
+    const int tc = (N + BC - 1) / BC;
+    const int tr_count = (N + BR - 1) / BR;
+    const int logical = xcd_remap(blockIdx.x, BH * tr_count);
+    const int bh = logical / tr_count;
+    // causal: the last query tiles see the most key tiles, so they go first
+    const int i = CAUSAL ? (tr_count - 1 - logical % tr_count) : (logical % tr_count);
+    const int q0 = i * BR;
+    const int j_end = CAUSAL ? min(tc, (min(q0 + BR, N) - 1) / BC + 1) : tc;
+
+    const __bf16* Kh = K + (size_t)bh * N * HD;
+    // transposing-read offsets (as in the dQ product of kernel A): keys
+    // 16 ks + 8 g + s4 (+4), queries of this wave's block, columns of its block
+    const int u_dq = qb * 8 + hh * 4 + (t16 & 3);
+    const int ods0 = toff(g * 8 + s4, u_dq), ods1 = toff(g * 8 + 4 + s4, u_dq);
+    const int kcol = db * 32 + hh * 16 + 4 * (t16 & 3);
+    const int okt0 = roff4<HD>(g * 8 + s4, kcol), okt1 = roff4<HD>(g * 8 + 4 + s4, kcol);
+
+    auto stage = [&](int jj, int buf) {
+        stage_bytes<S::DS_B, WAVES>(reinterpret_cast<const char*>(dSw + dst_tile(bh, i, jj, tr_count, tc)),
+                                    smem + S::off_ds + buf * S::DS_B, w, lane);
+        stage_rows<HD, BC, WAVES>(Kh, jj * BC, N, smem + S::off_k + buf * S::K_B, w, lane);
+    };
+    stage(0, 0);
+    __syncthreads();
+
+    f32x16 acc = zero16();
+    auto step = [&](int jj, auto bufc) {
+        constexpr int BUF = decltype(bufc)::value;
+        if (jj + 1 < j_end) stage(jj + 1, BUF ^ 1);
+        const __bf16* dST = reinterpret_cast<const __bf16*>(smem + S::off_ds + BUF * S::DS_B);
+        const __bf16* Ks = reinterpret_cast<const __bf16*>(smem + S::off_k + BUF * S::K_B);
+#pragma unroll
+        for (int ks = 0; ks < BC / 16; ++ks) {
+            const bf16x8 a = cat44(lds_read_tr(dST + ods0 + ks * 16 * BR),
+                                   lds_read_tr(dST + ods1 + ks * 16 * BR));
+            const bf16x8 b = cat44(lds_read_tr(Ks + okt0 + ks * 16 * HD),
+                                   lds_read_tr(Ks + okt1 + ks * 16 * HD));
+            acc = mfma32(a, b, acc);
+        }
+        __syncthreads();                        // next tiles landed; this buffer free
+    };
+    for (int jj = 0; jj < j_end; jj += 2) {
+        step(jj, std::integral_constant<int, 0>());
+        if (jj + 1 < j_end) step(jj + 1, std::integral_constant<int, 1>());
+    }
+
+    // ---- dQ = scale * acc, bf16 (RNE); rows past the end are not stored
+    __bf16* dQh = dQ + (size_t)bh * N * HD;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int row = q0 + qb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
+        if (row < N) dQh[(size_t)row * HD + db * 32 + l32] = (__bf16)(acc[r] * scale);
     }
 }
 
@@ -440,29 +519,59 @@ hipError_t launch_bwd_preprocess(const void* o, const void* dO, float* D, int BH
     return hipGetLastError();
 }
 
+// Workspace: [Lb BH x n_pad fp32][D BH x n_pad fp32][dS^T tiles BH x T_r x T_c
+// x (BC x BR) bf16].  Every dS^T tile the dQ kernel reads is written by the
+// dK/dV kernel first (causal: exactly the tiles with j <= i / 2).
+static size_t n_pad_of(int N) { return (size_t)((N + bwd::BR - 1) / bwd::BR) * bwd::BR; }
+
 size_t bwd_workspace_bytes(int BH, int N, int d) {
-    const size_t n_pad = (size_t)((N + bwd::BR - 1) / bwd::BR) * bwd::BR;
-    return (size_t)BH * n_pad * d * sizeof(float);
+    (void)d;
+    const size_t rows = (size_t)BH * n_pad_of(N);
+    const size_t tr = (N + bwd::BR - 1) / bwd::BR, tc = (N + bwd::BC - 1) / bwd::BC;
+    return 2 * rows * sizeof(float) + (size_t)BH * tr * tc * bwd::DST_EL * 2;
 }
 
 template <int HD, bool CAUSAL>
-static hipError_t launch_main(const void* q, const void* k, const void* v, const void* dO,
-                              const float* lse, const float* D, float* acc, void* dk, void* dv,
+static hipError_t launch_dkdv(const void* q, const void* k, const void* v, const void* dO,
+                              const float* Lb, const float* Dp, __bf16* dSw, void* dk, void* dv,
                               int BH, int N, int n_pad, float scale, hipStream_t stream) {
     using S = bwd::Smem<HD>;
-    auto kern = bwd::bwd_main_kernel<HD, CAUSAL>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, S::bytes);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    auto kern = bwd::bwd_dkdv_kernel<HD, CAUSAL>;
+    hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, S::bytes);
+    if (e != hipSuccess) return e;
     const int tc = (N + bwd::BC - 1) / bwd::BC;
     hipLaunchKernelGGL(kern, dim3(BH * tc), dim3(bwd::NT), S::bytes, stream, (const __bf16*)q,
-                       (const __bf16*)k, (const __bf16*)v, (const __bf16*)dO, lse, D, acc,
+                       (const __bf16*)k, (const __bf16*)v, (const __bf16*)dO, Lb, Dp, dSw,
                        (__bf16*)dk, (__bf16*)dv, BH, N, n_pad, scale);
     return hipGetLastError();
+}
+
+template <int HD, bool CAUSAL>
+static hipError_t launch_dq(const void* k, const __bf16* dSw, void* dq, int BH, int N, float scale,
+                            hipStream_t stream) {
+    using S = bwd::SmemQ<HD>;
+    auto kern = bwd::bwd_dq_kernel<HD, CAUSAL>;
+    hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, S::bytes);
+    if (e != hipSuccess) return e;
+    const int tr = (N + bwd::BR - 1) / bwd::BR;
+    hipLaunchKernelGGL(kern, dim3(BH * tr), dim3(HD / 16 * 64), S::bytes, stream, (const __bf16*)k,
+                       dSw, (__bf16*)dq, BH, N, scale);
+    return hipGetLastError();
+}
+
+template <int HD, bool CAUSAL>
+static hipError_t launch_pair(const void* q, const void* k, const void* v, const void* dO,
+                              const float* Lb, const float* Dp, __bf16* dSw, void* dq, void* dk,
+                              void* dv, int BH, int N, int n_pad, float scale, hipStream_t stream,
+                              hipEvent_t ev0, hipEvent_t ev1) {
+    hipError_t e;
+    if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
+    e = launch_dkdv<HD, CAUSAL>(q, k, v, dO, Lb, Dp, dSw, dk, dv, BH, N, n_pad, scale, stream);
+    if (e != hipSuccess) return e;
+    if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
+    return launch_dq<HD, CAUSAL>(k, dSw, dq, BH, N, scale, stream);
 }
 
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* dO, const float* lse,
@@ -470,32 +579,20 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* d
                       int d, bool causal, float scale, hipStream_t stream, hipEvent_t main_start,
                       hipEvent_t main_stop) {
     if ((long long)BH * N == 0) return hipSuccess;
-    const int n_pad = ((N + bwd::BR - 1) / bwd::BR) * bwd::BR;
-    float* acc = (float*)workspace;
-    const long long n4 = (long long)BH * n_pad * d / 4;
-    hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for(n4, 256 * 4, 4096)), dim3(256), 0, stream,
-                       (f32x4*)acc, n4);
+    const int n_pad = (int)n_pad_of(N);
+    const size_t rows = (size_t)BH * n_pad;
+    float* Lb = (float*)workspace;
+    float* Dp = Lb + rows;
+    __bf16* dSw = (__bf16*)(Dp + rows);
+    hipLaunchKernelGGL(bwd_prep_kernel, dim3(grid_for((long long)rows, 256, 4096)), dim3(256), 0,
+                       stream, Lb, Dp, lse, D, BH, N, n_pad);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (main_start && (e = hipEventRecord(main_start, stream)) != hipSuccess) return e;
-    if (d == 128) {
-        e = causal ? launch_main<128, true>(q, k, v, dO, lse, D, acc, dk, dv, BH, N, n_pad, scale, stream)
-                   : launch_main<128, false>(q, k, v, dO, lse, D, acc, dk, dv, BH, N, n_pad, scale, stream);
-    } else {
-        e = causal ? launch_main<64, true>(q, k, v, dO, lse, D, acc, dk, dv, BH, N, n_pad, scale, stream)
-                   : launch_main<64, false>(q, k, v, dO, lse, D, acc, dk, dv, BH, N, n_pad, scale, stream);
-    }
-    if (e != hipSuccess) return e;
-    if (main_stop && (e = hipEventRecord(main_stop, stream)) != hipSuccess) return e;
-    const long long chunks = (long long)BH * N * (d / 8);
-    if (d == 128) {
-        hipLaunchKernelGGL(dq_convert_kernel<128>, dim3(grid_for(chunks, 256 * 4, 8192)), dim3(256), 0,
-                           stream, acc, (__bf16*)dq, BH, N, n_pad, scale);
-    } else {
-        hipLaunchKernelGGL(dq_convert_kernel<64>, dim3(grid_for(chunks, 256 * 4, 8192)), dim3(256), 0,
-                           stream, acc, (__bf16*)dq, BH, N, n_pad, scale);
-    }
-    return hipGetLastError();
+    if (d == 128)
+        return causal ? launch_pair<128, true>(q, k, v, dO, Lb, Dp, dSw, dq, dk, dv, BH, N, n_pad, scale, stream, main_start, main_stop)
+                      : launch_pair<128, false>(q, k, v, dO, Lb, Dp, dSw, dq, dk, dv, BH, N, n_pad, scale, stream, main_start, main_stop);
+    return causal ? launch_pair<64, true>(q, k, v, dO, Lb, Dp, dSw, dq, dk, dv, BH, N, n_pad, scale, stream, main_start, main_stop)
+                  : launch_pair<64, false>(q, k, v, dO, Lb, Dp, dSw, dq, dk, dv, BH, N, n_pad, scale, stream, main_start, main_stop);
 }
 
 }  // namespace attn

@@ -71,8 +71,10 @@ attn_status attn_bwd_preprocess(const void* o, const void* dO, float* D, int B, 
                                 int d, void* stream);
 
 /*
- * Size in bytes of the workspace attn_bwd needs (an fp32 dQ accumulator with
- * the sequence rounded up to the 64-row query tile).  0 when B*H*N == 0.
+ * Size in bytes of the workspace attn_bwd needs: the row statistics L*log2(e)
+ * and D padded to the 64-row query tile (2 x B*H*ceil(N/64)*64 fp32), plus one
+ * bf16 128 x 64 dS^T tile per (batch*head, 64-row query tile, 128-key tile)
+ * (B*H*ceil(N/64)*ceil(N/128)*16 KiB).  0 when B*H*N == 0.
  */
 size_t attn_bwd_workspace_bytes(int B, int H, int N, int d);
 
@@ -80,9 +82,10 @@ size_t attn_bwd_workspace_bytes(int B, int H, int N, int d);
  * Fused backward (attention-backward page: the tiled backward pseudocode and
  * section "Main backward kernel"): recomputes P = exp(scale*S - L) tile by tile
  * and forms dV = P^T dO, dP = dO V^T, dS = P o (dP - D), dQ = scale*dS K and
- * dK = scale*dS^T Q.  dQ partials are added in fp32 into `workspace`
- * (cleared by this call) and rounded to bf16 by a second kernel on the same
- * stream.
+ * dK = scale*dS^T Q.  A first kernel (one workgroup per 128-key tile) produces
+ * dK and dV and stores each bf16 dS tile in `workspace`; a second kernel (one
+ * workgroup per 64-row query tile) reduces dQ = scale * sum_j dS_ij K_j in
+ * fp32 registers.  Both run on `stream`; no atomics are used.
  *   q, k, v, dO : bf16 [B, H, N, d], read only
  *   lse         : fp32 [B, H, N]  L from attn_fwd (natural log), read only
  *   D           : fp32 [B, H, N]  from attn_bwd_preprocess, read only
@@ -90,8 +93,7 @@ size_t attn_bwd_workspace_bytes(int B, int H, int N, int d);
  *   workspace   : device scratch of at least attn_bwd_workspace_bytes(B,H,N,d)
  *                 bytes (its content on entry is ignored and on exit unspecified)
  *   causal, scale : as for attn_fwd (must match the forward that produced lse)
- * dQ is reduced with fp32 atomics, so its low-order bits may differ between
- * runs; dK and dV are deterministic.
+ * dQ, dK and dV are deterministic (bitwise reproducible for the same inputs).
  */
 attn_status attn_bwd(const void* q, const void* k, const void* v, const void* dO,
                      const float* lse, const float* D, void* dq, void* dk, void* dv,
@@ -101,8 +103,8 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* dO
 /*
  * Same as attn_bwd, for profiling: when main_start / main_stop (hipEvent_t
  * created by the caller) are non-NULL they are recorded on `stream`
- * immediately before and after the fused backward kernel, so the caller can
- * time that kernel alone (hipEventElapsedTime) without a profiler.
+ * immediately before and after the dK/dV kernel (the dominant one), so the
+ * caller can time it alone (hipEventElapsedTime) without a profiler.
  */
 attn_status attn_bwd_timed(const void* q, const void* k, const void* v, const void* dO,
                            const float* lse, const float* D, void* dq, void* dk, void* dv,
