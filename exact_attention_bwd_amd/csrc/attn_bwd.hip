@@ -90,27 +90,33 @@ constexpr int BR = 64;           // query rows per iteration
 constexpr int NW = 8;            // wave64s per workgroup (2 per SIMD)
 constexpr int NT = NW * 64;
 
-// LDS tiles (all unpadded):
+// LDS tiles (all unpadded).  gfx950's LDS serves a 16-byte read for 16 lanes
+// per clock across 64 banks, i.e. one 256-byte bank line.
 //  * row-major [rows][HD] tiles (Q_i, dO_i, K_j, V_j): the 16-byte chunk c of
-//    row r lives at chunk c ^ rswz(r).  rswz takes the 8 values 0,2,4,6,1,3,5,7
-//    on any 8 consecutive rows, so the 16-byte operand reads of 8 consecutive
-//    rows hit 8 distinct bank groups, and on 4 consecutive rows it separates
-//    the two chunks a transposing read takes from each row.
+//    row r lives at chunk c ^ rswz<HD>(r).  For HD = 128 (one row per bank
+//    line) rswz takes 16 distinct values on any 16 consecutive rows, so the
+//    16-byte operand reads of 16 consecutive rows are conflict-free; its bits
+//    2..3 are r & 3, so the 4 rows x 4 chunks of one transposing read also land
+//    on 16 distinct chunks.  For HD = 64 (two rows per bank line) the same two
+//    properties hold per row parity.
 //  * dS^T [BC keys][BR queries] (workspace tiles, copied unchanged into the
 //    dQ kernel's LDS): the 8-byte unit u of row `key` lives at unit
-//    u ^ tswz(key), a bit permutation of the low 4 key bits, so 16 consecutive
-//    keys written at the same unit, and 4 keys x 4 units read by one
-//    transposing read, are all on distinct banks.
-__device__ __forceinline__ int rswz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+//    u ^ tswz(key), so 16 consecutive keys at the same unit, and 4 keys x 8
+//    units read by one transposing read, are on distinct banks.
+template <int HD>
+__device__ __forceinline__ int rswz(int r) {
+    return HD == 128 ? (((r & 3) << 2) | ((r >> 2) & 3))
+                     : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
 
 template <int HD>
 __device__ __forceinline__ int roff(int r, int c) {      // chunk c of row r (elements)
-    return r * HD + ((c ^ rswz(r)) << 3);
+    return r * HD + ((c ^ rswz<HD>(r)) << 3);
 }
 
 template <int HD>
 __device__ __forceinline__ int roff4(int r, int col) {   // 4 elements at col (multiple of 4)
-    return r * HD + ((((col >> 3) ^ rswz(r))) << 3) + (col & 4);
+    return r * HD + ((((col >> 3) ^ rswz<HD>(r))) << 3) + (col & 4);
 }
 
 __device__ __forceinline__ int tswz(int key) { return ((key & 3) << 2) | ((key >> 2) & 3); }
@@ -168,7 +174,7 @@ __device__ __forceinline__ void stage_rows(const __bf16* src, int row0, int N, c
         const int I = w * IPW + i;
         const int P = I * 64 + lane;                       // physical chunk
         const int r = P / CPR;
-        const int c = (P % CPR) ^ rswz(r);                 // logical chunk stored there
+        const int c = (P % CPR) ^ rswz<HD>(r);             // logical chunk stored there
         const int row = min(row0 + r, N - 1);
         dma16(src + (size_t)row * HD + c * 8, tile + I * 1024);
     }
@@ -249,10 +255,11 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     __bf16* const KB = reinterpret_cast<__bf16*>(smem + S::off_k);   // K; V at +BC*HD
     float* const LB = reinterpret_cast<float*>(smem + S::off_l);     // L buffers; D at +2*BR
 
-    // ---- loop-invariant per-lane LDS offsets (elements); every access below
-    //      is one of these plus a compile-time constant
+    // ---- loop-invariant per-lane LDS offsets (elements, relative to a tile);
+    //      every access below is one of these, XORed with a constant, plus a
+    //      compile-time constant
     // row reads of the A / B operands of S and dP: chunk 2ks+g of row rq / rk;
-    // k steps ks and ks + 4 differ by 8 chunks, which the swizzle leaves alone
+    // k steps ks and ks + 4 differ in chunk bit 3 only (offset ^ 64)
     int oq[4], okr[4];
     {
         const int rq = qh * 32 + l32, rk = kw * 32 + l32;
@@ -263,16 +270,11 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         }
     }
     // transposing reads of dO_i / Q_i (B operands of dV, dK): rows
-    // qh*32 + 16 k4 + 4g + s4 (+8), columns 32 db + 16 hh + 4 (t16 & 3); the
-    // row swizzle is the same for every k4 and for +8, and head-dim blocks
-    // 2, 3 sit 8 chunks after blocks 0, 1
-    int otr[2];
-    {
-        const int ra = qh * 32 + g * 4 + s4;
-#pragma unroll
-        for (int db = 0; db < 2; ++db)
-            otr[db] = roff4<HD>(ra, db * 32 + hh * 16 + 4 * (t16 & 3));
-    }
+    // qh*32 + 16 k4 + 4g + s4 and those + 8, columns 32 db + 16 hh + 4 (t16 & 3).
+    // The row swizzle is the same for every k4; rows + 8 flip chunk bit 1
+    // (offset ^ 16) and head-dim block db flips chunk bits 2..3 by db
+    // (offset ^ (db << 5)).
+    const int otr = roff4<HD>(qh * 32 + g * 4 + s4, hh * 16 + 4 * (t16 & 3));
     // dS^T stores: this lane's key, units qh*8 + 2 rr + g of the workspace tile
     int ow[4];
 #pragma unroll
@@ -304,27 +306,37 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const float sl2 = scale * kLog2e;
     const int key_lane = k0 + kw * 32 + l32;     // this lane's key (accumulator column)
 
-    auto iteration = [&](int it, auto bufc) {
-        constexpr int BUF = decltype(bufc)::value;
-        const __bf16* Qs = QB + BUF * TILE_EL;
-        const __bf16* dOs = QB + (2 + BUF) * TILE_EL;
-        const float* Ls = LB + BUF * BR;
-        const float* Ds = LB + (2 + BUF) * BR;
+    for (int it = it0, buf = 0; it < tr_count; ++it, buf ^= 1) {
         const int q0 = it * BR;
-        if (it + 1 < tr_count) stage_tile(it + 1, BUF ^ 1);     // lands during this iteration
+        if (it + 1 < tr_count) stage_tile(it + 1, buf ^ 1);     // lands during this iteration
+        const __bf16* Qs = QB + buf * TILE_EL;
+        const __bf16* dOs = Qs + 2 * TILE_EL;
+        const float* Ls = LB + buf * BR;
+        const float* Ds = Ls + 2 * BR;
 
         // ---- S = Q K^T, dP = dO V^T: this wave's 32 queries x 32 keys
         f32x16 s = zero16(), dp = zero16();
 #pragma unroll
         for (int ks = 0; ks < KSD; ++ks) {
-            const int hi = (ks >> 2) * 64;
-            s = mfma32(lds_read16(Qs + oq[ks & 3] + hi), lds_read16(KB + okr[ks & 3] + hi), s);
-            dp = mfma32(lds_read16(dOs + oq[ks & 3] + hi),
-                        lds_read16(KB + BC * HD + okr[ks & 3] + hi), dp);
+            const int xo = (ks >> 2) * 64;          // chunk bit 3 for k steps 4..7
+            const int oa = oq[ks & 3] ^ xo, ob = okr[ks & 3] ^ xo;
+            s = mfma32(lds_read16(Qs + oa), lds_read16(KB + ob), s);
+            dp = mfma32(lds_read16(dOs + oa), lds_read16(KB + BC * HD + ob), dp);
         }
 
+        // ---- masking, only where this wave's keys reach past its first query
+        //      row (causal diagonal) or past the end (ragged last key tile)
+        const bool need_mask =
+            (k0 + BC > N) || (CAUSAL && (k0 + kw * 32 + 31 > q0 + qh * 32));
+        if (__builtin_expect(need_mask, 0)) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int q = q0 + ol + (r >> 2) * 8 + (r & 3);
+                const bool masked = (key_lane >= N) || (CAUSAL && key_lane > q);
+                s[r] = masked ? -__builtin_inff() : s[r];
+            }
+        }
         // ---- P = exp(scale*S - L), dS = P o (dP - D); masked entries give 0
-        const bool need_mask = (k0 + BC > N) || (CAUSAL && (k0 + kw * 32 + 31 > q0 + qh * 32));
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
             const f32x4 lv = *reinterpret_cast<const f32x4*>(Ls + ol + rr * 8);
@@ -332,13 +344,7 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = rr * 4 + e;
-                float x = __builtin_fmaf(s[r], sl2, -lv[e]);
-                if (need_mask) {
-                    const bool masked = (key_lane >= N) ||
-                                        (CAUSAL && key_lane > q0 + ol + rr * 8 + e);
-                    x = masked ? -__builtin_inff() : x;
-                }
-                const float p = __builtin_amdgcn_exp2f(x);
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -lv[e]));
                 s[r] = p;
                 dp[r] = p * (dp[r] - dd[e]);
             }
@@ -351,12 +357,13 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         //      operands are read transposed from the row-major dO_i, Q_i tiles
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-            const int o = otr[db & 1] + (db >> 1) * 64;
+            const int o0 = otr ^ (db << 5);
+            const int o8 = (otr + 8 * HD) ^ (db << 5) ^ 16;
 #pragma unroll
             for (int k4 = 0; k4 < 2; ++k4) {
                 const int rk = k4 * 16 * HD;
-                const bf16x8 bo = cat44(lds_read_tr(dOs + o + rk), lds_read_tr(dOs + o + rk + 8 * HD));
-                const bf16x8 bq = cat44(lds_read_tr(Qs + o + rk), lds_read_tr(Qs + o + rk + 8 * HD));
+                const bf16x8 bo = cat44(lds_read_tr(dOs + o0 + rk), lds_read_tr(dOs + o8 + rk));
+                const bf16x8 bq = cat44(lds_read_tr(Qs + o0 + rk), lds_read_tr(Qs + o8 + rk));
                 dv[db] = mfma32(k4 ? pa1 : pa0, bo, dv[db]);
                 dk[db] = mfma32(k4 ? ds1 : ds0, bq, dk[db]);
             }
@@ -370,11 +377,6 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         *reinterpret_cast<bf16x4*>(dst + ow[1]) = __builtin_shufflevector(ds0, ds0, 4, 5, 6, 7);
         *reinterpret_cast<bf16x4*>(dst + ow[2]) = __builtin_shufflevector(ds1, ds1, 0, 1, 2, 3);
         *reinterpret_cast<bf16x4*>(dst + ow[3]) = __builtin_shufflevector(ds1, ds1, 4, 5, 6, 7);
-    };
-
-    for (int it = it0; it < tr_count; it += 2) {
-        iteration(it, std::integral_constant<int, 0>());
-        if (it + 1 < tr_count) iteration(it + 1, std::integral_constant<int, 1>());
     }
 
     // ---- epilogue: the two waves sharing 32 keys (qh = 0, 1) add their partial
