@@ -161,6 +161,35 @@ __device__ __forceinline__ void dma4(const void* src, void* lds_base) {
     __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 4, 0, 0);
 }
 
+// Raw buffer resource over `bytes` bytes from `base`: loads past the end read
+// as zero, stores past the end are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+// Buffer -> LDS copy: lane l of the wave writes its BYTES at lds_base + l * BYTES.
+__device__ __forceinline__ void bdma16(__amdgpu_buffer_rsrc_t r, int voff, void* lds_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16,
+                                             voff, 0, 0, 0);
+}
+
+__device__ __forceinline__ void bdma4(__amdgpu_buffer_rsrc_t r, int voff, void* lds_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 4,
+                                             voff, 0, 0, 0);
+}
+
+// Copy ROWS rows of a [*, HD] bf16 tensor, starting at the descriptor's base,
+// into a swizzled LDS tile with WAVES waves (rows past the descriptor's end
+// arrive as zeros, whose contributions are masked).  voff[i] are the per-lane
+// byte offsets of instruction i (see stage_offsets).
+template <int HD, int ROWS, int WAVES>
+__device__ __forceinline__ void stage_rows_b(__amdgpu_buffer_rsrc_t r, const int* voff, char* tile,
+                                             int w) {
+    constexpr int IPW = ROWS * (HD / 8) / 64 / WAVES;
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) bdma16(r, voff[i], tile + (w * IPW + i) * 1024);
+}
+
 // Copy rows [row0, row0 + ROWS) of a [*, HD] bf16 tensor into a swizzled LDS
 // tile with WAVES waves; rows at or past N re-read row N - 1 (finite values
 // whose contributions are masked to zero).
@@ -177,6 +206,20 @@ __device__ __forceinline__ void stage_rows(const __bf16* src, int row0, int N, c
         const int c = (P % CPR) ^ rswz<HD>(r);             // logical chunk stored there
         const int row = min(row0 + r, N - 1);
         dma16(src + (size_t)row * HD + c * 8, tile + I * 1024);
+    }
+}
+
+// Per-lane source byte offsets for stage_rows_b: the physical chunk this lane
+// writes belongs to row r, logical chunk (p ^ rswz(r)).
+template <int HD, int ROWS, int WAVES>
+__device__ __forceinline__ void stage_offsets(int* voff, int w, int lane) {
+    constexpr int CPR = HD / 8;
+    constexpr int IPW = ROWS * CPR / 64 / WAVES;
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+        const int P = (w * IPW + i) * 64 + lane;
+        const int r = P / CPR;
+        voff[i] = (r * HD + (((P % CPR) ^ rswz<HD>(r)) << 3)) * 2;
     }
 }
 
@@ -200,6 +243,13 @@ __device__ __forceinline__ size_t dst_tile(int bh, int i, int j, int tr, int tc)
     return ((size_t)((size_t)bh * tr + i) * tc + j) * DST_EL;
 }
 
+// Workspace image of K_j as ready-made B operands of dQ = dS K: for each
+// 32-column head-dim block db and 16-key step ks, a 1 KiB block in which lane l
+// holds K[16 ks + 8 (l / 32) + e][32 db + l % 32], e = 0..7.
+__device__ __forceinline__ size_t kimg_tile(int bh, int j, int tc, int HD) {
+    return ((size_t)bh * tc + j) * BC * HD;
+}
+
 // ----------------------------------------------------------------------------
 // Kernel A: one workgroup per (batch*head, 128-key tile j).  Walks the query
 // tiles i (from the diagonal tile when causal), recomputes S_ij and P_ij from
@@ -220,7 +270,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
 void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                      const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                      const float* __restrict__ Lb, const float* __restrict__ Dp,
-                     __bf16* __restrict__ dSw, __bf16* __restrict__ dK,
+                     __bf16* __restrict__ dSw, __bf16* __restrict__ Kimg, __bf16* __restrict__ dK,
                      __bf16* __restrict__ dV, int BH, int N, int n_pad, float scale) {
     using S = Smem<HD>;
     constexpr int KSD = HD / 16;                 // k steps over the head dim
@@ -283,18 +333,48 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 
     const int it0 = CAUSAL ? (k0 / BR) : 0;
 
-    // ---- K_j, V_j and the first Q_i / dO_i tile (with its L, D rows) to LDS
+    // ---- K_j, V_j and the first Q_i / dO_i tile (with its L, D rows) to LDS.
+    //      Each copy's row offset lives in the buffer descriptor (scalar); the
+    //      per-lane offsets are loop-invariant; rows past N read as zero.
+    constexpr int ROWB = HD * 2;                 // bytes per row
+    int vo_q[BR * (HD / 8) / 64 / NW], vo_k[BC * (HD / 8) / 64 / NW];
+    stage_offsets<HD, BR, NW>(vo_q, w, lane);
+    stage_offsets<HD, BC, NW>(vo_k, w, lane);
     auto stage_tile = [&](int it, int buf) {
         const int q0 = it * BR;
-        stage_rows<HD, BR, NW>(Qh, q0, N, smem + S::off_q + buf * S::TILE, w, lane);
-        stage_rows<HD, BR, NW>(dOh, q0, N, smem + S::off_do + buf * S::TILE, w, lane);
-        if (w == 0) dma4(Lbh + q0 + lane, smem + S::off_l + buf * BR * 4);
-        if (w == 1) dma4(Dph + q0 + lane, smem + S::off_d + buf * BR * 4);
+        const int bytes = (N - q0) * ROWB;
+        stage_rows_b<HD, BR, NW>(make_rsrc(Qh + (size_t)q0 * HD, bytes), vo_q,
+                                 smem + S::off_q + buf * S::TILE, w);
+        stage_rows_b<HD, BR, NW>(make_rsrc(dOh + (size_t)q0 * HD, bytes), vo_q,
+                                 smem + S::off_do + buf * S::TILE, w);
+        if (w == 0) bdma4(make_rsrc(Lbh + q0, BR * 4), lane * 4, smem + S::off_l + buf * BR * 4);
+        if (w == 1) bdma4(make_rsrc(Dph + q0, BR * 4), lane * 4, smem + S::off_d + buf * BR * 4);
     };
-    stage_rows<HD, BC, NW>(K + head, k0, N, smem + S::off_k, w, lane);
-    stage_rows<HD, BC, NW>(V + head, k0, N, smem + S::off_v, w, lane);
+    {
+        const int bytes = (N - k0) * ROWB;
+        stage_rows_b<HD, BC, NW>(make_rsrc(K + head + (size_t)k0 * HD, bytes), vo_k, smem + S::off_k, w);
+        stage_rows_b<HD, BC, NW>(make_rsrc(V + head + (size_t)k0 * HD, bytes), vo_k, smem + S::off_v, w);
+    }
     stage_tile(it0, 0);
     __syncthreads();
+
+    // ---- K_j image for the dQ kernel: 2 * DB * 8 blocks of 1 KiB, spread over
+    //      the waves; each block is two transposing reads of the K tile
+    {
+        constexpr int NBLK = DB * (BC / 16);
+        const __amdgpu_buffer_rsrc_t kr = make_rsrc(Kimg + kimg_tile(bh, j, tc, HD), BC * HD * 2);
+#pragma unroll
+        for (int b = 0; b < NBLK / NW; ++b) {
+            const int blk = w * (NBLK / NW) + b;
+            const int bdb = blk / (BC / 16), bks = blk % (BC / 16);
+            const int key = bks * 16 + g * 8 + s4;
+            const int col = bdb * 32 + hh * 16 + 4 * (t16 & 3);
+            const bf16x8 v = cat44(lds_read_tr(KB + roff4<HD>(key, col)),
+                                   lds_read_tr(KB + roff4<HD>(key + 4, col)));
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), kr,
+                                                   (blk * 64 + lane) * 16, 0, 0);
+        }
+    }
 
     f32x16 dv[DB], dk[DB];
 #pragma unroll
@@ -372,11 +452,13 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         // stores go after the barrier so that its wait for the tile copies does
         // not also wait for them
         __syncthreads();
-        __bf16* dst = dSw + dst_tile(bh, it, j, tr_count, tc);
-        *reinterpret_cast<bf16x4*>(dst + ow[0]) = __builtin_shufflevector(ds0, ds0, 0, 1, 2, 3);
-        *reinterpret_cast<bf16x4*>(dst + ow[1]) = __builtin_shufflevector(ds0, ds0, 4, 5, 6, 7);
-        *reinterpret_cast<bf16x4*>(dst + ow[2]) = __builtin_shufflevector(ds1, ds1, 0, 1, 2, 3);
-        *reinterpret_cast<bf16x4*>(dst + ow[3]) = __builtin_shufflevector(ds1, ds1, 4, 5, 6, 7);
+        const __amdgpu_buffer_rsrc_t dsr =
+            make_rsrc(dSw + dst_tile(bh, it, j, tr_count, tc), DST_EL * 2);
+        const u32x4 d0 = __builtin_bit_cast(u32x4, ds0), d1 = __builtin_bit_cast(u32x4, ds1);
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{d0[0], d0[1]}, dsr, ow[0] * 2, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{d0[2], d0[3]}, dsr, ow[1] * 2, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{d1[0], d1[1]}, dsr, ow[2] * 2, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{d1[2], d1[3]}, dsr, ow[3] * 2, 0, 0);
     }
 
     // ---- epilogue: the two waves sharing 32 keys (qh = 0, 1) add their partial
@@ -407,34 +489,29 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 }
 
 // ----------------------------------------------------------------------------
-// Kernel B: dQ_i = scale * sum_j dS_ij K_j, one workgroup per (batch*head,
-// 64-row query tile i).  The dS^T tiles written by kernel A and the K_j tiles
-// are copied into LDS one tile ahead; each wave owns one 32 x 32 block of dQ_i
-// and accumulates it over all key tiles in registers, reading both operands
-// transposed.  No atomics: the reduction over key tiles happens in registers.
+// Kernel B: dQ_i = scale * sum_j dS_ij K_j, one workgroup of 4 wave64s per
+// (batch*head, 64-row query tile i).  The dS^T tiles written by kernel A are
+// copied into an LDS double buffer one step ahead and read transposed (A
+// operands); the B operands come straight from the K image in registers, one
+// step ahead.  With 32 KiB of LDS per workgroup several workgroups share a CU,
+// which hides the memory latency.  The reduction over key tiles happens in
+// fp32 registers (no atomics).
 // ----------------------------------------------------------------------------
-template <int HD> struct SmemQ {
-    static constexpr int DS_B = DST_EL * 2;               // one dS^T tile (bytes)
-    static constexpr int K_B = BC * HD * 2;               // one K tile (bytes)
-    static constexpr int off_ds = 0;                      // two buffers
-    static constexpr int off_k = 2 * DS_B;                // two buffers
-    static constexpr int bytes = off_k + 2 * K_B;
-};
+constexpr int QW = 4;                            // waves per dQ workgroup
 
 template <int HD, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(HD / 16 * 64, HD / 16 * 64)))
-void bwd_dq_kernel(const __bf16* __restrict__ K, const __bf16* __restrict__ dSw,
+__global__ __attribute__((amdgpu_flat_work_group_size(QW * 64, QW * 64)))
+void bwd_dq_kernel(const __bf16* __restrict__ Kimg, const __bf16* __restrict__ dSw,
                    __bf16* __restrict__ dQ, int BH, int N, float scale) {
-    using S = SmemQ<HD>;
     constexpr int DB = HD / 32;
-    constexpr int WAVES = 2 * DB;                // one 32 x 32 dQ block per wave
-    extern __shared__ __attribute__((aligned(16))) char smem[];
+    constexpr int TQ = 2 * DB / QW;              // 32 x 32 dQ blocks per wave (2 or 1)
+    constexpr int DS_B = DST_EL * 2;             // one dS^T tile (bytes)
+    __shared__ __attribute__((aligned(16))) char smem[2 * DS_B];
 
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
-    const int qb = w / DB;                       // query block (32 rows) of the tile
-    const int db = w % DB;                       // head-dim block (32 columns)
-    const int l32 = lane & 31;
+    const int db = w % DB;                       // this wave's 32 head-dim columns
+    const int qb0 = (TQ == 2) ? 0 : (w / DB);    // its first 32-row query block
     const int g = lane >> 5;
     const int t16 = lane & 15;
     const int hh = (lane >> 4) & 1;
@@ -449,49 +526,73 @@ void bwd_dq_kernel(const __bf16* __restrict__ K, const __bf16* __restrict__ dSw,
     const int q0 = i * BR;
     const int j_end = CAUSAL ? min(tc, (min(q0 + BR, N) - 1) / BC + 1) : tc;
 
-    const __bf16* Kh = K + (size_t)bh * N * HD;
-    // transposing-read offsets (as in the dQ product of kernel A): keys
-    // 16 ks + 8 g + s4 (+4), queries of this wave's block, columns of its block
-    const int u_dq = qb * 8 + hh * 4 + (t16 & 3);
-    const int ods0 = toff(g * 8 + s4, u_dq), ods1 = toff(g * 8 + 4 + s4, u_dq);
-    const int kcol = db * 32 + hh * 16 + 4 * (t16 & 3);
-    const int okt0 = roff4<HD>(g * 8 + s4, kcol), okt1 = roff4<HD>(g * 8 + 4 + s4, kcol);
+    // transposing-read offsets into a dS^T tile: keys 16 ks + 8 g + s4 (+4),
+    // queries of query block qb (plus a constant per ks)
+    int ods[TQ][2];
+#pragma unroll
+    for (int t = 0; t < TQ; ++t) {
+        const int u = (qb0 + t) * 8 + hh * 4 + (t16 & 3);
+        ods[t][0] = toff(g * 8 + s4, u);
+        ods[t][1] = toff(g * 8 + 4 + s4, u);
+    }
 
     auto stage = [&](int jj, int buf) {
-        stage_bytes<S::DS_B, WAVES>(reinterpret_cast<const char*>(dSw + dst_tile(bh, i, jj, tr_count, tc)),
-                                    smem + S::off_ds + buf * S::DS_B, w, lane);
-        stage_rows<HD, BC, WAVES>(Kh, jj * BC, N, smem + S::off_k + buf * S::K_B, w, lane);
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(dSw + dst_tile(bh, i, jj, tr_count, tc), DS_B);
+#pragma unroll
+        for (int k = 0; k < DS_B / 1024 / QW; ++k) {
+            const int I = w * (DS_B / 1024 / QW) + k;
+            bdma16(r, I * 1024 + lane * 16, smem + buf * DS_B + I * 1024);
+        }
     };
+    auto load_k = [&](int jj, bf16x8* kb) {
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(Kimg + kimg_tile(bh, jj, tc, HD), BC * HD * 2);
+#pragma unroll
+        for (int ks = 0; ks < BC / 16; ++ks)
+            kb[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    r, ((db * (BC / 16) + ks) * 64 + lane) * 16, 0, 0));
+    };
+
+    bf16x8 kcur[BC / 16], knext[BC / 16];
     stage(0, 0);
+    load_k(0, kcur);
     __syncthreads();
 
-    f32x16 acc = zero16();
-    auto step = [&](int jj, auto bufc) {
-        constexpr int BUF = decltype(bufc)::value;
-        if (jj + 1 < j_end) stage(jj + 1, BUF ^ 1);
-        const __bf16* dST = reinterpret_cast<const __bf16*>(smem + S::off_ds + BUF * S::DS_B);
-        const __bf16* Ks = reinterpret_cast<const __bf16*>(smem + S::off_k + BUF * S::K_B);
+    f32x16 acc[TQ];
+#pragma unroll
+    for (int t = 0; t < TQ; ++t) acc[t] = zero16();
+    for (int jj = 0, buf = 0; jj < j_end; ++jj, buf ^= 1) {
+        const bool more = jj + 1 < j_end;
+        if (more) {
+            stage(jj + 1, buf ^ 1);
+            load_k(jj + 1, knext);
+        }
+        const __bf16* dST = reinterpret_cast<const __bf16*>(smem + buf * DS_B);
 #pragma unroll
         for (int ks = 0; ks < BC / 16; ++ks) {
-            const bf16x8 a = cat44(lds_read_tr(dST + ods0 + ks * 16 * BR),
-                                   lds_read_tr(dST + ods1 + ks * 16 * BR));
-            const bf16x8 b = cat44(lds_read_tr(Ks + okt0 + ks * 16 * HD),
-                                   lds_read_tr(Ks + okt1 + ks * 16 * HD));
-            acc = mfma32(a, b, acc);
+#pragma unroll
+            for (int t = 0; t < TQ; ++t) {
+                const bf16x8 a = cat44(lds_read_tr(dST + ods[t][0] + ks * 16 * BR),
+                                       lds_read_tr(dST + ods[t][1] + ks * 16 * BR));
+                acc[t] = mfma32(a, kcur[ks], acc[t]);
+            }
         }
-        __syncthreads();                        // next tiles landed; this buffer free
-    };
-    for (int jj = 0; jj < j_end; jj += 2) {
-        step(jj, std::integral_constant<int, 0>());
-        if (jj + 1 < j_end) step(jj + 1, std::integral_constant<int, 1>());
+        __syncthreads();                        // next tile landed; this buffer free
+        if (more) {
+#pragma unroll
+            for (int ks = 0; ks < BC / 16; ++ks) kcur[ks] = knext[ks];
+        }
     }
 
     // ---- dQ = scale * acc, bf16 (RNE); rows past the end are not stored
     __bf16* dQh = dQ + (size_t)bh * N * HD;
+    const int l32 = lane & 31;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int row = q0 + qb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-        if (row < N) dQh[(size_t)row * HD + db * 32 + l32] = (__bf16)(acc[r] * scale);
+    for (int t = 0; t < TQ; ++t) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = q0 + (qb0 + t) * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
+            if (row < N) dQh[(size_t)row * HD + db * 32 + l32] = (__bf16)(acc[t][r] * scale);
+        }
     }
 }
 
@@ -522,21 +623,22 @@ hipError_t launch_bwd_preprocess(const void* o, const void* dO, float* D, int BH
 }
 
 // Workspace: [Lb BH x n_pad fp32][D BH x n_pad fp32][dS^T tiles BH x T_r x T_c
-// x (BC x BR) bf16].  Every dS^T tile the dQ kernel reads is written by the
-// dK/dV kernel first (causal: exactly the tiles with j <= i / 2).
+// x (BC x BR) bf16][K image BH x T_c x (BC x d) bf16].  Every dS^T tile the dQ
+// kernel reads is written by the dK/dV kernel first (causal: exactly the tiles
+// with j <= i / 2), and so is every K image tile.
 static size_t n_pad_of(int N) { return (size_t)((N + bwd::BR - 1) / bwd::BR) * bwd::BR; }
 
 size_t bwd_workspace_bytes(int BH, int N, int d) {
-    (void)d;
     const size_t rows = (size_t)BH * n_pad_of(N);
     const size_t tr = (N + bwd::BR - 1) / bwd::BR, tc = (N + bwd::BC - 1) / bwd::BC;
-    return 2 * rows * sizeof(float) + (size_t)BH * tr * tc * bwd::DST_EL * 2;
+    return 2 * rows * sizeof(float) + (size_t)BH * tr * tc * bwd::DST_EL * 2 +
+           (size_t)BH * tc * bwd::BC * d * 2;
 }
 
 template <int HD, bool CAUSAL>
 static hipError_t launch_dkdv(const void* q, const void* k, const void* v, const void* dO,
-                              const float* Lb, const float* Dp, __bf16* dSw, void* dk, void* dv,
-                              int BH, int N, int n_pad, float scale, hipStream_t stream) {
+                              const float* Lb, const float* Dp, __bf16* dSw, __bf16* kimg, void* dk,
+                              void* dv, int BH, int N, int n_pad, float scale, hipStream_t stream) {
     using S = bwd::Smem<HD>;
     auto kern = bwd::bwd_dkdv_kernel<HD, CAUSAL>;
     hipError_t e = hipFuncSetAttribute((const void*)kern,
@@ -544,36 +646,31 @@ static hipError_t launch_dkdv(const void* q, const void* k, const void* v, const
     if (e != hipSuccess) return e;
     const int tc = (N + bwd::BC - 1) / bwd::BC;
     hipLaunchKernelGGL(kern, dim3(BH * tc), dim3(bwd::NT), S::bytes, stream, (const __bf16*)q,
-                       (const __bf16*)k, (const __bf16*)v, (const __bf16*)dO, Lb, Dp, dSw,
+                       (const __bf16*)k, (const __bf16*)v, (const __bf16*)dO, Lb, Dp, dSw, kimg,
                        (__bf16*)dk, (__bf16*)dv, BH, N, n_pad, scale);
     return hipGetLastError();
 }
 
 template <int HD, bool CAUSAL>
-static hipError_t launch_dq(const void* k, const __bf16* dSw, void* dq, int BH, int N, float scale,
-                            hipStream_t stream) {
-    using S = bwd::SmemQ<HD>;
-    auto kern = bwd::bwd_dq_kernel<HD, CAUSAL>;
-    hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, S::bytes);
-    if (e != hipSuccess) return e;
+static hipError_t launch_dq(const __bf16* kimg, const __bf16* dSw, void* dq, int BH, int N,
+                            float scale, hipStream_t stream) {
     const int tr = (N + bwd::BR - 1) / bwd::BR;
-    hipLaunchKernelGGL(kern, dim3(BH * tr), dim3(HD / 16 * 64), S::bytes, stream, (const __bf16*)k,
-                       dSw, (__bf16*)dq, BH, N, scale);
+    hipLaunchKernelGGL((bwd::bwd_dq_kernel<HD, CAUSAL>), dim3(BH * tr), dim3(bwd::QW * 64), 0, stream,
+                       kimg, dSw, (__bf16*)dq, BH, N, scale);
     return hipGetLastError();
 }
 
 template <int HD, bool CAUSAL>
 static hipError_t launch_pair(const void* q, const void* k, const void* v, const void* dO,
-                              const float* Lb, const float* Dp, __bf16* dSw, void* dq, void* dk,
-                              void* dv, int BH, int N, int n_pad, float scale, hipStream_t stream,
-                              hipEvent_t ev0, hipEvent_t ev1) {
+                              const float* Lb, const float* Dp, __bf16* dSw, __bf16* kimg, void* dq,
+                              void* dk, void* dv, int BH, int N, int n_pad, float scale,
+                              hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
     hipError_t e;
     if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
-    e = launch_dkdv<HD, CAUSAL>(q, k, v, dO, Lb, Dp, dSw, dk, dv, BH, N, n_pad, scale, stream);
+    e = launch_dkdv<HD, CAUSAL>(q, k, v, dO, Lb, Dp, dSw, kimg, dk, dv, BH, N, n_pad, scale, stream);
     if (e != hipSuccess) return e;
     if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
-    return launch_dq<HD, CAUSAL>(k, dSw, dq, BH, N, scale, stream);
+    return launch_dq<HD, CAUSAL>(kimg, dSw, dq, BH, N, scale, stream);
 }
 
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* dO, const float* lse,
@@ -586,15 +683,17 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* d
     float* Lb = (float*)workspace;
     float* Dp = Lb + rows;
     __bf16* dSw = (__bf16*)(Dp + rows);
+    const size_t tr = (N + bwd::BR - 1) / bwd::BR, tc = (N + bwd::BC - 1) / bwd::BC;
+    __bf16* kimg = dSw + (size_t)BH * tr * tc * bwd::DST_EL;
     hipLaunchKernelGGL(bwd_prep_kernel, dim3(grid_for((long long)rows, 256, 4096)), dim3(256), 0,
                        stream, Lb, Dp, lse, D, BH, N, n_pad);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (d == 128)
-        return causal ? launch_pair<128, true>(q, k, v, dO, Lb, Dp, dSw, dq, dk, dv, BH, N, n_pad, scale, stream, main_start, main_stop)
-                      : launch_pair<128, false>(q, k, v, dO, Lb, Dp, dSw, dq, dk, dv, BH, N, n_pad, scale, stream, main_start, main_stop);
-    return causal ? launch_pair<64, true>(q, k, v, dO, Lb, Dp, dSw, dq, dk, dv, BH, N, n_pad, scale, stream, main_start, main_stop)
-                  : launch_pair<64, false>(q, k, v, dO, Lb, Dp, dSw, dq, dk, dv, BH, N, n_pad, scale, stream, main_start, main_stop);
+        return causal ? launch_pair<128, true>(q, k, v, dO, Lb, Dp, dSw, kimg, dq, dk, dv, BH, N, n_pad, scale, stream, main_start, main_stop)
+                      : launch_pair<128, false>(q, k, v, dO, Lb, Dp, dSw, kimg, dq, dk, dv, BH, N, n_pad, scale, stream, main_start, main_stop);
+    return causal ? launch_pair<64, true>(q, k, v, dO, Lb, Dp, dSw, kimg, dq, dk, dv, BH, N, n_pad, scale, stream, main_start, main_stop)
+                  : launch_pair<64, false>(q, k, v, dO, Lb, Dp, dSw, kimg, dq, dk, dv, BH, N, n_pad, scale, stream, main_start, main_stop);
 }
 
 }  // namespace attn

@@ -72,9 +72,10 @@ attn_status attn_bwd_preprocess(const void* o, const void* dO, float* D, int B, 
 
 /*
  * Size in bytes of the workspace attn_bwd needs: the row statistics L*log2(e)
- * and D padded to the 64-row query tile (2 x B*H*ceil(N/64)*64 fp32), plus one
+ * and D padded to the 64-row query tile (2 x B*H*ceil(N/64)*64 fp32), one
  * bf16 128 x 64 dS^T tile per (batch*head, 64-row query tile, 128-key tile)
- * (B*H*ceil(N/64)*ceil(N/128)*16 KiB).  0 when B*H*N == 0.
+ * (B*H*ceil(N/64)*ceil(N/128)*16 KiB), and a bf16 copy of K rearranged as
+ * matrix-core operands (B*H*ceil(N/128)*128*d*2 bytes).  0 when B*H*N == 0.
  */
 size_t attn_bwd_workspace_bytes(int B, int H, int N, int d);
 

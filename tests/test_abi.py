@@ -47,10 +47,12 @@ def test_library_is_gfx950_code(ea):
 
 def test_workspace_size(ea):
     # two fp32 row statistics (rows rounded up to 64) + one bf16 128x64 dS^T
-    # tile per (batch*head, 64-row query tile, 128-key tile)
+    # tile per (batch*head, 64-row query tile, 128-key tile) + a bf16 image of K
+    # per 128-key tile
     tile = 128 * 64 * 2
-    assert ea.attn_bwd_workspace_bytes(8, 16, 4096, 128) == 2 * 128 * 4096 * 4 + 128 * 64 * 32 * tile
-    assert ea.attn_bwd_workspace_bytes(1, 1, 100, 64) == 2 * 128 * 4 + 2 * 1 * tile
+    assert ea.attn_bwd_workspace_bytes(8, 16, 4096, 128) == (
+        2 * 128 * 4096 * 4 + 128 * 64 * 32 * tile + 128 * 32 * 128 * 128 * 2)
+    assert ea.attn_bwd_workspace_bytes(1, 1, 100, 64) == 2 * 128 * 4 + 2 * 1 * tile + 128 * 64 * 2
     assert ea.attn_bwd_workspace_bytes(0, 16, 4096, 128) == 0
     assert ea.attn_bwd_workspace_bytes(1, 1, 128, 96) == 0                  # unsupported d
 
