@@ -123,6 +123,69 @@ def _traffic():
 
 
 # ----------------------------------------------------------------------------
+# HBM traffic from rocprofv3 counter passes
+# ----------------------------------------------------------------------------
+COPY_BYTES = 1 << 30             # the calibration copy moves 1 GiB each way
+MAIN_KERNEL = "bwd_dkdv_kernel"
+
+
+def copy_calibration():
+    """A plain device-to-device copy of COPY_BYTES, three times: the copy kernel
+    reads and writes exactly COPY_BYTES, which scales the TCC byte counters."""
+    import torch
+    n = COPY_BYTES // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": COPY_BYTES, "copy_bytes_written": COPY_BYTES}), flush=True)
+
+
+def _counter_mean(csv_path, counter, kernel_substr, biggest=False):
+    import csv
+    vals = []
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter and kernel_substr in r["Kernel_Name"]:
+                vals.append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"{csv_path}: no {counter} rows for a kernel named *{kernel_substr}*")
+    return max(vals) if biggest else sum(vals) / len(vals)
+
+
+def write_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, commands):
+    """Turn four rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE and
+    WRITE_SIZE of the bench, then of the calibration copy) into the committed
+    per-dispatch HBM traffic of the main kernel."""
+    fetch = _counter_mean(fetch_csv, "FETCH_SIZE", MAIN_KERNEL)
+    write = _counter_mean(write_csv, "WRITE_SIZE", MAIN_KERNEL)
+    cfetch = _counter_mean(copy_fetch_csv, "FETCH_SIZE", "copyBuffer", biggest=True)
+    cwrite = _counter_mean(copy_write_csv, "WRITE_SIZE", "copyBuffer", biggest=True)
+    fs = COPY_BYTES / (cfetch * 1024.0)
+    ws = COPY_BYTES / (cwrite * 1024.0)
+    out = {
+        "kernel": MAIN_KERNEL,
+        "source_sha256": _sources_sha(),
+        "fetch_size_kib_per_dispatch": fetch,
+        "write_size_kib_per_dispatch": write,
+        "copy_fetch_size_kib": cfetch,
+        "copy_write_size_kib": cwrite,
+        "copy_bytes": COPY_BYTES,
+        "fetch_scale": fs,
+        "write_scale": ws,
+        "hbm_read_bytes_per_dispatch": fetch * 1024.0 * fs,
+        "hbm_write_bytes_per_dispatch": write * 1024.0 * ws,
+        "hbm_bytes_per_dispatch": fetch * 1024.0 * fs + write * 1024.0 * ws,
+        "commands": commands,
+    }
+    with open(COUNTERS_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
+
+
+# ----------------------------------------------------------------------------
 def cpu_baseline(inp, cfg, budget_s):
     """The fp64 oracle, timed on whole heads of the same workload."""
     import numpy as np
@@ -136,7 +199,7 @@ def cpu_baseline(inp, cfg, budget_s):
     BH = cfg.B * cfg.H
     per_head = bwd_flops(1, 1, cfg.N, cfg.d, cfg.causal)
     done, t_total = 0, 0.0
-    while done < min(BH, 16) and (done == 0 or t_total < budget_s):
+    while done < BH and (done == 0 or t_total < budget_s):
         sl = lambda n: bf16_bits_to_f64(inp[n].reshape(BH, cfg.N, cfg.d)[done])  # noqa: E731
         q, k, v, do = sl("q"), sl("k"), sl("v"), sl("do")
         t0 = time.perf_counter()
@@ -157,16 +220,29 @@ def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only the 1 GiB calibration copy (for the TCC byte counters)")
+    ap.add_argument("--write-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="summarise rocprofv3 --pmc FETCH_SIZE/WRITE_SIZE passes into the counters file (no GPU)")
+    ap.add_argument("--commands", nargs="*", default=[], help="the profiling commands, recorded with --write-counters")
     args = ap.parse_args(argv)
+
+    if args.write_counters:
+        write_counters(*args.write_counters, commands=args.commands)
+        return 0
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
               f"(--gpus {args.gpus} is not supported)", file=sys.stderr)
         return 2
+
+    if args.copy_calibration:
+        copy_calibration()
+        return 0
 
     import torch
     import exact_attention_bwd_amd as ea
