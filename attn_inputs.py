@@ -96,9 +96,18 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
 
     Inputs must be finite (the generators never produce NaN or Inf)."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32)
-    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
-    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+    u = x.reshape(-1).view(np.uint32)
+    out = np.empty(u.shape, dtype=np.uint16)
+    step = 1 << 20                               # chunks that stay in cache
+    for s in range(0, u.size, step):
+        c = u[s:s + step]
+        t = c >> np.uint32(16)
+        t &= np.uint32(1)
+        t += np.uint32(0x7FFF)                   # round half to even
+        t += c
+        t >>= np.uint32(16)
+        out[s:s + step] = t
+    return out.reshape(x.shape)
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:

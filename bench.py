@@ -216,6 +216,103 @@ def cpu_baseline(inp, cfg, budget_s):
     }
 
 
+SPARSE_MAIN_SHARE = (2 * 576 + 2 * 512) * 2 / (2 * (3 * 576 + 2 * 512))   # S, dP, dV, dK of 5 products
+
+
+def sparse_valid_pairs(topk_len) -> int:
+    return int(sum(int(x) for x in topk_len))
+
+
+def bench_sparse(args, cfg):
+    """Top-k sparse backward (attn_bwd_preprocess + attn_sparse_bwd), same
+    timing protocol as the dense benchmark."""
+    import numpy as np
+    import torch
+    import exact_attention_bwd_amd as ea
+    from attn_inputs import make_sparse_inputs
+
+    dev = torch.device("cuda:0")
+    print(f"[bench] {cfg.name}: Hq{cfg.Hq} Nq{cfg.Nq} Nkv{cfg.Nkv} dqk{cfg.dqk} dv{cfg.dv} topk{cfg.topk}: inputs",
+          file=sys.stderr, flush=True)
+    inp = make_sparse_inputs(cfg)
+
+    def up(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v, do = (up(inp[n]) for n in ("q", "k", "v", "do"))
+    idx = torch.from_numpy(inp["idx"]).to(dev)
+    tl = torch.from_numpy(inp["topk_len"]).to(dev)
+    o, lse = ea.attn_sparse_fwd(q, k, v, idx, tl, cfg.scale)
+    D = torch.empty((cfg.Hq, cfg.Nq), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty((ea.attn_sparse_bwd_workspace_bytes(cfg.Hq, cfg.Nq, cfg.Nkv, cfg.topk, cfg.dqk, cfg.dv),),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    ev = HipEvents()
+
+    def step(events=None):
+        ea.attn_bwd_preprocess(o[None], do[None], D=D[None])
+        ea.attn_sparse_bwd(q, k, v, do, lse, D, idx, tl, cfg.scale, dq=dq, dk=dk, dv=dv, workspace=ws,
+                           main_events=events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    pairs = [(ev.create(), ev.create()) for _ in range(K)]
+    t0, t1 = ev.create(), ev.create()
+    ev.rt.hipEventRecord(ctypes.c_void_p(t0), ctypes.c_void_p(stream.cuda_stream))
+    for i in range(K):
+        step(pairs[i])
+    ev.rt.hipEventRecord(ctypes.c_void_p(t1), ctypes.c_void_p(stream.cuda_stream))
+    torch.cuda.synchronize()
+    ms_step = ev.elapsed_ms(t0, t1) / K
+    main_ms = [ev.elapsed_ms(a, b) for a, b in pairs]
+    main_avg = sum(main_ms) / K
+    # forward on its own
+    ev.rt.hipEventRecord(ctypes.c_void_p(t0), ctypes.c_void_p(stream.cuda_stream))
+    for _ in range(K):
+        ea.attn_sparse_fwd(q, k, v, idx, tl, cfg.scale, o=o, lse=lse)
+    ev.rt.hipEventRecord(ctypes.c_void_p(t1), ctypes.c_void_p(stream.cuda_stream))
+    torch.cuda.synchronize()
+    fwd_ms = ev.elapsed_ms(t0, t1) / K
+    for a, b in pairs:
+        ev.destroy(a)
+        ev.destroy(b)
+    nominal = sparse_bwd_flops(cfg.Hq, cfg.Nq, cfg.topk, cfg.dqk, cfg.dv)
+    valid = 2.0 * cfg.Hq * sparse_valid_pairs(inp["topk_len"]) * (3 * cfg.dqk + 2 * cfg.dv)
+    main_fl = SPARSE_MAIN_SHARE * valid
+    value = tflops(nominal, ms_step)
+    line = {
+        "metric": "sparse top-k attn bwd effective TFLOPS (2·H·N·topk·(3·d_qk+2·d_v))",
+        "value": round(value, 3),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"top-k sparse attention backward (preprocess + backward) Hq{cfg.Hq} "
+                               f"Nq{cfg.Nq} Nkv{cfg.Nkv} d_qk{cfg.dqk} d_v{cfg.dv} topk{cfg.topk} bf16, "
+                               f"seed {cfg.seed}"},
+        "valid_pair_tflops": round(tflops(valid, ms_step), 3),
+        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 3),
+        "main_kernel": {"name": "sbwd_main_kernel", "ms": round(main_avg, 5),
+                        "tflops": round(tflops(main_fl, main_avg), 3)},
+        "rest_ms": round(ms_step - main_avg, 5),
+        "forward": {"ms": round(fwd_ms, 5),
+                    "tflops": round(tflops(2.0 * cfg.Hq * sparse_valid_pairs(inp["topk_len"])
+                                           * (cfg.dqk + cfg.dv), fwd_ms), 3)},
+        "pages_b200_ms": 1.533,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -248,6 +345,9 @@ def main(argv=None):
     import exact_attention_bwd_amd as ea
     from attn_inputs import DENSE_CONFIGS, make_dense_inputs
 
+    from attn_inputs import SPARSE_CONFIGS
+    if args.config in SPARSE_CONFIGS:
+        return bench_sparse(args, SPARSE_CONFIGS[args.config])
     cfg = DENSE_CONFIGS[args.config]
     B, H, N, d = cfg.B, cfg.H, cfg.N, cfg.d
     dev = torch.device("cuda:0")

@@ -18,7 +18,8 @@ import torch
 
 __all__ = [
     "attn_fwd", "attn_bwd_preprocess", "attn_bwd", "attn_bwd_workspace_bytes",
-    "attention_backward", "lib_path", "AttnError", "version",
+    "attention_backward", "attn_sparse_fwd", "attn_sparse_bwd", "attn_sparse_bwd_workspace_bytes",
+    "lib_path", "AttnError", "version",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -49,6 +50,14 @@ def _load():
     lib.attn_bwd.restype = i
     lib.attn_bwd_timed.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, vp, vp, vp]
     lib.attn_bwd_timed.restype = i
+    lib.attn_sparse_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+    lib.attn_sparse_fwd.restype = i
+    lib.attn_sparse_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.attn_sparse_bwd_workspace_bytes.restype = sz
+    lib.attn_sparse_bwd.argtypes = [vp] * 12 + [sz, i, i, i, i, i, i, f, vp]
+    lib.attn_sparse_bwd.restype = i
+    lib.attn_sparse_bwd_timed.argtypes = [vp] * 12 + [sz, i, i, i, i, i, i, f, vp, vp, vp]
+    lib.attn_sparse_bwd_timed.restype = i
     lib.attn_last_error.argtypes = []
     lib.attn_last_error.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -173,3 +182,78 @@ def attention_backward(q, k, v, do, o, lse, causal: bool, scale: float | None = 
     """The whole backward of the method: preprocess (D) then the fused backward."""
     D = attn_bwd_preprocess(o, do, stream=stream)
     return attn_bwd(q, k, v, do, lse, D, causal, scale, workspace=workspace, stream=stream)
+
+
+# ---------------------------------------------------------------------------
+# Top-k sparse attention (d_qk = 576, d_v = 512, heads in groups of 64)
+# ---------------------------------------------------------------------------
+def _dev(x, dtype, shape, name):
+    if x.dtype != dtype or not x.is_cuda or not x.is_contiguous() or tuple(x.shape) != tuple(shape):
+        raise ValueError(f"{name} must be a contiguous {dtype} device tensor of shape {tuple(shape)}, "
+                         f"got {x.dtype} {tuple(x.shape)}")
+
+
+def _sparse_dims(q, k, v, idx):
+    if q.dim() != 3 or k.dim() != 2 or v.dim() != 2 or idx.dim() != 2:
+        raise ValueError("expected q [Hq, Nq, dqk], k [Nkv, dqk], v [Nkv, dv], idx [Nq, topk]")
+    Hq, Nq, dqk = q.shape
+    Nkv, dvd = v.shape
+    topk = idx.shape[1]
+    _dev(q, torch.bfloat16, (Hq, Nq, dqk), "q")
+    _dev(k, torch.bfloat16, (Nkv, dqk), "k")
+    _dev(v, torch.bfloat16, (Nkv, dvd), "v")
+    _dev(idx, torch.int32, (Nq, topk), "idx")
+    return Hq, Nq, Nkv, dqk, dvd, topk
+
+
+def attn_sparse_fwd(q, k, v, idx, topk_len=None, scale: float | None = None, o=None, lse=None,
+                    stream=None):
+    """Sparse forward.  Returns (o bf16 [Hq, Nq, dv], lse fp32 [Hq, Nq])."""
+    Hq, Nq, Nkv, dqk, dvd, topk = _sparse_dims(q, k, v, idx)
+    if topk_len is not None:
+        _dev(topk_len, torch.int32, (Nq,), "topk_len")
+    if scale is None:
+        scale = 1.0 / math.sqrt(dqk)
+    o = torch.empty((Hq, Nq, dvd), dtype=torch.bfloat16, device=q.device) if o is None else o
+    lse = torch.empty((Hq, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _dev(o, torch.bfloat16, (Hq, Nq, dvd), "o")
+    _dev(lse, torch.float32, (Hq, Nq), "lse")
+    _check(_lib.attn_sparse_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(topk_len), _ptr(o),
+                                _ptr(lse), Hq, Nq, Nkv, dqk, dvd, topk, float(scale), _stream(stream)))
+    return o, lse
+
+
+def attn_sparse_bwd_workspace_bytes(Hq: int, Nq: int, Nkv: int, topk: int, dqk: int = 576,
+                                    dv: int = 512) -> int:
+    return int(_lib.attn_sparse_bwd_workspace_bytes(Hq, Nq, Nkv, dqk, dv, topk))
+
+
+def attn_sparse_bwd(q, k, v, do, lse, D, idx, topk_len=None, scale: float | None = None,
+                    dq=None, dk=None, dv=None, workspace=None, stream=None, main_events=None):
+    """Sparse backward.  Returns (dq [Hq, Nq, dqk], dk [Nkv, dqk], dv [Nkv, dv]), bf16."""
+    Hq, Nq, Nkv, dqk, dvd, topk = _sparse_dims(q, k, v, idx)
+    _dev(do, torch.bfloat16, (Hq, Nq, dvd), "dO")
+    _dev(lse, torch.float32, (Hq, Nq), "lse")
+    _dev(D, torch.float32, (Hq, Nq), "D")
+    if topk_len is not None:
+        _dev(topk_len, torch.int32, (Nq,), "topk_len")
+    if scale is None:
+        scale = 1.0 / math.sqrt(dqk)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _dev(dq, torch.bfloat16, (Hq, Nq, dqk), "dq")
+    _dev(dk, torch.bfloat16, (Nkv, dqk), "dk")
+    _dev(dv, torch.bfloat16, (Nkv, dvd), "dv")
+    need = attn_sparse_bwd_workspace_bytes(Hq, Nq, Nkv, topk, dqk, dvd)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    args = [_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(D), _ptr(idx), _ptr(topk_len),
+            _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, Hq, Nq, Nkv, dqk, dvd, topk,
+            float(scale), _stream(stream)]
+    if main_events is None:
+        _check(_lib.attn_sparse_bwd(*args))
+    else:
+        _check(_lib.attn_sparse_bwd_timed(*args, *(ctypes.c_void_p(e) for e in main_events)))
+    return dq, dk, dv

@@ -80,7 +80,8 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
 attn_status attn_bwd_preprocess(const void* o, const void* dO, float* D, int B, int H, int N,
                                 int d, void* stream) {
     bool empty = false;
-    CHECK(check_shape(B, H, N, d, &empty));
+    // the sparse path's O and dO are 512 wide
+    CHECK(check_shape(B, H, N, d == 512 ? 128 : d, &empty));
     if (empty) return ok();
     CHECK(check_ptr(o, "o", 16));
     CHECK(check_ptr(dO, "dO", 16));
@@ -128,6 +129,98 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* dO
                      int causal, float scale, void* stream) {
     return attn_bwd_timed(q, k, v, dO, lse, D, dq, dk, dv, workspace, workspace_bytes, B, H, N, d,
                           causal, scale, stream, nullptr, nullptr);
+}
+
+// ---------------------------------------------------------------------------
+// Top-k sparse attention
+// ---------------------------------------------------------------------------
+namespace {
+
+attn_status check_sparse(int Hq, int Nq, int Nkv, int dqk, int dv, int topk, bool bwd) {
+    if (Hq < 0 || Nq < 0 || Nkv < 0 || topk < 0)
+        return fail(ATTN_ERR_INVALID_ARG, "negative size Hq=%d Nq=%d Nkv=%d topk=%d", Hq, Nq, Nkv, topk);
+    if (dqk != 576 || dv != 512)
+        return fail(ATTN_ERR_UNSUPPORTED, "sparse head dims (d_qk=%d, d_v=%d) are not (576, 512)", dqk, dv);
+    if (Hq % 64 != 0) return fail(ATTN_ERR_UNSUPPORTED, "Hq=%d is not a multiple of 64", Hq);
+    if (Nkv > (1 << 20)) return fail(ATTN_ERR_UNSUPPORTED, "Nkv=%d above 1048576", Nkv);
+    if (bwd && Nkv > 16384) return fail(ATTN_ERR_UNSUPPORTED, "sparse backward: Nkv=%d above 16384", Nkv);
+    if ((long long)Nq * topk > 0x7fffffffLL || (long long)Nq * (Hq / 64) > 0x7fffffffLL)
+        return fail(ATTN_ERR_UNSUPPORTED, "sizes too large Nq=%d topk=%d Hq=%d", Nq, topk, Hq);
+    return ATTN_OK;
+}
+
+}  // namespace
+
+attn_status attn_sparse_fwd(const void* q, const void* k, const void* v, const int* idx,
+                            const int* topk_len, void* o, float* lse, int Hq, int Nq, int Nkv,
+                            int dqk, int dv, int topk, float scale, void* stream) {
+    CHECK(check_sparse(Hq, Nq, Nkv, dqk, dv, topk, false));
+    if (!isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "scale is not finite");
+    if ((long long)Hq * Nq == 0) return ok();
+    CHECK(check_ptr(q, "q", 16));
+    CHECK(check_ptr(o, "o", 16));
+    CHECK(check_ptr(lse, "lse", 4));
+    if (Nkv > 0) {
+        CHECK(check_ptr(k, "k", 16));
+        CHECK(check_ptr(v, "v", 16));
+    }
+    if (topk > 0) CHECK(check_ptr(idx, "idx", 4));
+    if (topk_len) CHECK(check_ptr(topk_len, "topk_len", 4));
+    return hip_status(attn::launch_sparse_fwd(q, k, v, idx, topk_len, o, lse, Hq, Nq, Nkv, topk,
+                                              scale, (hipStream_t)stream),
+                      "attn_sparse_fwd launch");
+}
+
+size_t attn_sparse_bwd_workspace_bytes(int Hq, int Nq, int Nkv, int dqk, int dv, int topk) {
+    if (check_sparse(Hq, Nq, Nkv, dqk, dv, topk, true) != ATTN_OK) return 0;
+    if ((long long)Hq * Nq == 0 && Nkv == 0) return 0;
+    return attn::sparse_bwd_workspace_bytes(Hq, Nq, Nkv, topk);
+}
+
+attn_status attn_sparse_bwd_timed(const void* q, const void* k, const void* v, const void* dO,
+                                  const float* lse, const float* D, const int* idx,
+                                  const int* topk_len, void* dq, void* dk, void* dv,
+                                  void* workspace, size_t workspace_bytes, int Hq, int Nq, int Nkv,
+                                  int dqk, int dvd, int topk, float scale, void* stream,
+                                  void* main_start, void* main_stop) {
+    CHECK(check_sparse(Hq, Nq, Nkv, dqk, dvd, topk, true));
+    if (!isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "scale is not finite");
+    const bool rows = (long long)Hq * Nq > 0;
+    if (!rows && Nkv == 0) return ok();
+    if (rows) {
+        CHECK(check_ptr(q, "q", 16));
+        CHECK(check_ptr(dO, "dO", 16));
+        CHECK(check_ptr(lse, "lse", 4));
+        CHECK(check_ptr(D, "D", 4));
+        CHECK(check_ptr(dq, "dq", 16));
+    }
+    if (Nkv > 0) {
+        CHECK(check_ptr(k, "k", 16));
+        CHECK(check_ptr(v, "v", 16));
+        CHECK(check_ptr(dk, "dk", 16));
+        CHECK(check_ptr(dv, "dv", 16));
+    }
+    if ((long long)Nq * topk > 0) CHECK(check_ptr(idx, "idx", 4));
+    if (topk_len) CHECK(check_ptr(topk_len, "topk_len", 4));
+    CHECK(check_ptr(workspace, "workspace", 16));
+    const size_t need = attn::sparse_bwd_workspace_bytes(Hq, Nq, Nkv, topk);
+    if (workspace_bytes < need)
+        return fail(ATTN_ERR_WORKSPACE, "workspace is %zu bytes, %zu needed", workspace_bytes, need);
+    return hip_status(attn::launch_sparse_bwd(q, k, v, dO, lse, D, idx, topk_len, dq, dk, dv,
+                                              workspace, Hq, Nq, Nkv, topk, scale,
+                                              (hipStream_t)stream, (hipEvent_t)main_start,
+                                              (hipEvent_t)main_stop),
+                      "attn_sparse_bwd launch");
+}
+
+attn_status attn_sparse_bwd(const void* q, const void* k, const void* v, const void* dO,
+                            const float* lse, const float* D, const int* idx, const int* topk_len,
+                            void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                            int Hq, int Nq, int Nkv, int dqk, int dvd, int topk, float scale,
+                            void* stream) {
+    return attn_sparse_bwd_timed(q, k, v, dO, lse, D, idx, topk_len, dq, dk, dv, workspace,
+                                 workspace_bytes, Hq, Nq, Nkv, dqk, dvd, topk, scale, stream,
+                                 nullptr, nullptr);
 }
 
 const char* attn_last_error(void) { return g_err; }

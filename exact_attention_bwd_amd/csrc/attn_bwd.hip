@@ -149,45 +149,6 @@ template <int HD> struct Smem {
     static_assert(xchg <= off_l, "partial exchange must fit below L / D");
 };
 
-// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
-// lane i receives element i % 4 of the 8 bytes addressed by lanes i / 4,
-// 4 + i / 4, 8 + i / 4 and 12 + i / 4.  If lane t of the group addresses row
-// r0 + t / 4, columns c0 + 4 (t % 4) .. + 3 of a row-major tile, lane i gets
-// column c0 + i of rows r0 .. r0 + 3.
-__device__ __forceinline__ bf16x4 lds_read_tr(const __bf16* p) {
-    typedef short s16x4 __attribute__((ext_vector_type(4)));
-    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4*)(p));
-    return __builtin_bit_cast(bf16x4, v);
-}
-
-// Direct global -> LDS copy: lane l of the wave writes its `bytes` (4 or 16)
-// at lds_base + l * bytes; lds_base is the same for the whole wave.
-__device__ __forceinline__ void dma16(const void* src, void* lds_base) {
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
-}
-
-__device__ __forceinline__ void dma4(const void* src, void* lds_base) {
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 4, 0, 0);
-}
-
-// Raw buffer resource over `bytes` bytes from `base`: loads past the end read
-// as zero, stores past the end are dropped.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
-}
-
-// Buffer -> LDS copy: lane l of the wave writes its BYTES at lds_base + l * BYTES.
-__device__ __forceinline__ void bdma16(__amdgpu_buffer_rsrc_t r, int voff, void* lds_base) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16,
-                                             voff, 0, 0, 0);
-}
-
-__device__ __forceinline__ void bdma4(__amdgpu_buffer_rsrc_t r, int voff, void* lds_base) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 4,
-                                             voff, 0, 0, 0);
-}
-
 // Copy ROWS rows of a [*, HD] bf16 tensor, starting at the descriptor's base,
 // into a swizzled LDS tile with WAVES waves (rows past the descriptor's end
 // arrive as zeros, whose contributions are masked).  voff[i] are the per-lane
@@ -622,7 +583,10 @@ hipError_t launch_bwd_preprocess(const void* o, const void* dO, float* D, int BH
                                  hipStream_t stream) {
     const long long rows = (long long)BH * N;
     if (rows == 0) return hipSuccess;
-    if (d == 128) {
+    if (d == 512) {
+        hipLaunchKernelGGL(bwd_preprocess_kernel<512>, dim3(grid_for(rows, 4, 8192)), dim3(256), 0,
+                           stream, (const __bf16*)o, (const __bf16*)dO, D, rows);
+    } else if (d == 128) {
         hipLaunchKernelGGL(bwd_preprocess_kernel<128>, dim3(grid_for(rows, 16, 8192)), dim3(256), 0,
                            stream, (const __bf16*)o, (const __bf16*)dO, D, rows);
     } else {

@@ -21,4 +21,17 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* d
                       int d, bool causal, float scale, hipStream_t stream,
                       hipEvent_t main_start = nullptr, hipEvent_t main_stop = nullptr);
 
+// Top-k sparse attention (d_qk = 576, d_v = 512, heads in groups of 64).
+size_t sparse_bwd_workspace_bytes(int Hq, int Nq, int Nkv, int topk);
+
+hipError_t launch_sparse_fwd(const void* q, const void* k, const void* v, const int* idx,
+                             const int* tlen, void* o, float* lse, int Hq, int Nq, int Nkv,
+                             int topk, float scale, hipStream_t stream);
+
+hipError_t launch_sparse_bwd(const void* q, const void* k, const void* v, const void* dO,
+                             const float* lse, const float* D, const int* idx, const int* tlen,
+                             void* dq, void* dk, void* dv, void* workspace, int Hq, int Nq, int Nkv,
+                             int topk, float scale, hipStream_t stream,
+                             hipEvent_t main_start = nullptr, hipEvent_t main_stop = nullptr);
+
 }  // namespace attn

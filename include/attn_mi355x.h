@@ -66,6 +66,8 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
  * Backward preprocess (attention-backward page, section "Precomputing D"):
  *   D_i = sum_c dO_ic * O_ic, accumulated in fp32 from the bf16 inputs.
  *   o, dO : bf16 [B, H, N, d], read only;  D : fp32 [B, H, N], written.
+ *   d may also be 512: the O and dO of the sparse path ([Hq, Nq, 512], i.e.
+ *   B = 1, H = Hq, N = Nq) use this same entry point.
  */
 attn_status attn_bwd_preprocess(const void* o, const void* dO, float* D, int B, int H, int N,
                                 int d, void* stream);
@@ -112,6 +114,72 @@ attn_status attn_bwd_timed(const void* q, const void* k, const void* v, const vo
                            void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
                            int causal, float scale, void* stream, void* main_start,
                            void* main_stop);
+
+/*
+ * ---------------------------------------------------------------------------
+ * Top-k sparse attention (cudnn-frontend PR #684, "Improve performance of
+ * SM100 DSA backward kernel": DSA attention with one shared K/V head).
+ * Query row i attends, for every head, to the keys its index list names:
+ *     S_h,i,s = scale * Q[h,i] . K[idx[i,s]]   for the valid slots s of row i
+ *     P = softmax over the valid slots,  O[h,i] = sum_s P_h,i,s V[idx[i,s]]
+ * and the backward applies the dense formulas above to that gathered set, with
+ *     dK[j] = scale * sum over (h, i, s : idx[i,s] = j) of dS_h,i,s Q[h,i]
+ *     dV[j] =         sum over (h, i, s : idx[i,s] = j) of P_h,i,s dO[h,i].
+ * Shapes (all dense, row-major, bf16 unless noted):
+ *   q  [Hq, Nq, dqk]    k  [Nkv, dqk]    v  [Nkv, dv]
+ *   o, dO  [Hq, Nq, dv]     lse, D  fp32 [Hq, Nq]
+ *   idx    int32 [Nq, topk]: key indices of each row
+ *   topk_len  int32 [Nq] or NULL: number of leading slots of each row in use
+ *             (clamped to [0, topk]; NULL = all topk)
+ * A slot is valid when it is in use and its index lies in [0, Nkv); other
+ * slots (e.g. -1 padding) are ignored.  A row with no valid slot gets O = 0,
+ * L = -inf and zero gradients.  Supported: dqk = 576, dv = 512, Hq a multiple
+ * of 64 (heads are processed in groups of 64 that share each gathered K/V
+ * row), Nkv <= 1048576 (backward: Nkv <= 16384).  Pointer alignment as for the
+ * dense calls; idx and topk_len 4-byte aligned.
+ */
+attn_status attn_sparse_fwd(const void* q, const void* k, const void* v, const int* idx,
+                            const int* topk_len, void* o, float* lse, int Hq, int Nq, int Nkv,
+                            int dqk, int dv, int topk, float scale, void* stream);
+
+/*
+ * Workspace of attn_sparse_bwd: a per-row-block key histogram
+ * (ceil(Nq/64) x Nkv int32), key offsets (Nkv + 1 int32), the transposed pair
+ * list (Nq x topk int32), dS (Nq x Hq/64 x ceil(topk/128)*128 x 64 bf16) and
+ * each (row, head group, slot)'s dK/dV contribution (Nq x Hq/64 x topk x 1088
+ * fp32; 9.1 GB at Hq = 64, Nq = 4096, topk = 512), each 256-byte aligned.
+ * 0 for unsupported or empty problems.
+ */
+size_t attn_sparse_bwd_workspace_bytes(int Hq, int Nq, int Nkv, int dqk, int dv, int topk);
+
+/*
+ * Sparse backward.  lse from attn_sparse_fwd, D from attn_bwd_preprocess(o,
+ * dO, D, 1, Hq, Nq, 512).  Writes dq [Hq, Nq, dqk], dk [Nkv, dqk], dv [Nkv, dv]
+ * (every key row, zero for keys no row selected).  Kernels, all on `stream`:
+ * a counting-sort transpose of the index lists (per key, its (row, slot)
+ * pairs in row order), a per-row kernel that recomputes S, P, dP, dS for the
+ * 64 heads of a group and stores dS and each slot's dK/dV contribution, a
+ * per-row dQ kernel, and a per-key reduction of the contributions in that
+ * fixed order.  No floating-point atomics: results are reproducible, except
+ * that a key repeated within one row's list is summed in an unspecified order.
+ */
+attn_status attn_sparse_bwd(const void* q, const void* k, const void* v, const void* dO,
+                            const float* lse, const float* D, const int* idx, const int* topk_len,
+                            void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                            int Hq, int Nq, int Nkv, int dqk, int dv_dim, int topk, float scale,
+                            void* stream);
+
+/*
+ * attn_sparse_bwd with caller-created hipEvent_t main_start / main_stop (may
+ * be NULL) recorded on `stream` immediately before and after the per-row
+ * backward kernel, for timing it alone.
+ */
+attn_status attn_sparse_bwd_timed(const void* q, const void* k, const void* v, const void* dO,
+                                  const float* lse, const float* D, const int* idx,
+                                  const int* topk_len, void* dq, void* dk, void* dv,
+                                  void* workspace, size_t workspace_bytes, int Hq, int Nq, int Nkv,
+                                  int dqk, int dv_dim, int topk, float scale, void* stream,
+                                  void* main_start, void* main_stop);
 
 /* Message describing the last non-OK status returned on this thread ("" if none). */
 const char* attn_last_error(void);

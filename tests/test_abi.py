@@ -100,3 +100,48 @@ def test_empty_problems_are_noops(ea):
 
 def test_version(ea):
     assert "gfx950" in ea.version()
+
+
+def test_sparse_validation_errors_do_not_launch(ea):
+    lib = _raw(ea)
+    p = ctypes.c_void_p(4096)
+    f = ctypes.c_float
+    # unsupported head dims / head count
+    assert lib.attn_sparse_fwd(p, p, p, p, None, p, p, 64, 16, 16, 512, 512, 8, f(0.1), None) == -2
+    assert b"576" in lib.attn_last_error()
+    assert lib.attn_sparse_fwd(p, p, p, p, None, p, p, 32, 16, 16, 576, 512, 8, f(0.1), None) == -2
+    # negative size, non-finite scale
+    assert lib.attn_sparse_fwd(p, p, p, p, None, p, p, 64, -1, 16, 576, 512, 8, f(0.1), None) == -1
+    assert lib.attn_sparse_fwd(p, p, p, p, None, p, p, 64, 16, 16, 576, 512, 8, f(float("nan")), None) == -1
+    # misaligned index list
+    assert lib.attn_sparse_fwd(p, p, p, ctypes.c_void_p(4098), None, p, p, 64, 16, 16, 576, 512, 8,
+                               f(0.1), None) == -1
+    # backward key limit and workspace size
+    assert lib.attn_sparse_bwd_workspace_bytes(64, 16, 20000, 576, 512, 8) == 0
+    need = lib.attn_sparse_bwd_workspace_bytes(64, 16, 16, 576, 512, 8)
+    assert lib.attn_sparse_bwd(p, p, p, p, p, p, p, None, p, p, p, p, need - 1, 64, 16, 16, 576, 512, 8,
+                               f(0.1), None) == -4
+    assert lib.attn_sparse_bwd(p, p, p, p, p, p, p, None, p, p, p, p, 1 << 40, 64, 16, 20000, 576, 512, 8,
+                               f(0.1), None) == -2
+
+
+def test_sparse_workspace_size(ea):
+    # per-row-block key counts, key offsets, pair list, dS (64 heads per slot,
+    # slots padded to 128) and the fp32 dK/dV contribution of every slot
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    got = ea.attn_sparse_bwd_workspace_bytes(64, 4096, 4096, 512)
+    assert got == (al(64 * 4096 * 4) + al(4097 * 4) + al(4096 * 512 * 4) + al(4096 * 512 * 64 * 2)
+                   + al(4096 * 512 * 1088 * 4))
+    assert ea.attn_sparse_bwd_workspace_bytes(128, 300, 280, 100) == (
+        al(5 * 280 * 4) + al(281 * 4) + al(300 * 100 * 4) + al(300 * 2 * 128 * 64 * 2)
+        + al(300 * 2 * 100 * 1088 * 4))
+    assert ea.attn_sparse_bwd_workspace_bytes(0, 0, 0, 8) == 0
+
+
+def test_sparse_empty_is_noop(ea):
+    lib = _raw(ea)
+    f = ctypes.c_float
+    assert lib.attn_sparse_fwd(None, None, None, None, None, None, None, 0, 16, 16, 576, 512, 8, f(0.1), None) == 0
+    assert lib.attn_sparse_fwd(None, None, None, None, None, None, None, 64, 0, 16, 576, 512, 8, f(0.1), None) == 0
+    assert lib.attn_sparse_bwd(None, None, None, None, None, None, None, None, None, None, None, None, 0,
+                               64, 0, 0, 576, 512, 8, f(0.1), None) == 0
