@@ -250,7 +250,7 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     extern __shared__ __attribute__((aligned(16))) char smem[];
 
     const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
+    const int w = wave_id();
     const int kw = w & 3;                        // this wave's 32 keys of the 128
     const int qh = w >> 2;                       // this wave's 32 query rows of the 64
     const int l32 = lane & 31;
@@ -313,7 +313,7 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     stage_offsets<HD, BC, NW>(vo_k, w, lane);
     auto stage_tile = [&](int it, int buf) {
         const int q0 = it * BR;
-        const int bytes = (N - q0) * ROWB;
+        const int bytes = min(N - q0, BR) * ROWB;
         stage_rows_b<HD, BR, NW>(make_rsrc(Qh + (size_t)q0 * HD, bytes), vo_q,
                                  smem + S::off_q + buf * S::TILE, w);
         stage_rows_b<HD, BR, NW>(make_rsrc(dOh + (size_t)q0 * HD, bytes), vo_q,
@@ -322,7 +322,7 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         if (w == 1) bdma4(make_rsrc(Dph + q0, BR * 4), lane * 4, smem + S::off_d + buf * BR * 4);
     };
     {
-        const int bytes = (N - k0) * ROWB;
+        const int bytes = min(N - k0, BC) * ROWB;
         stage_rows_b<HD, BC, NW>(make_rsrc(K + head + (size_t)k0 * HD, bytes), vo_k, smem + S::off_k, w);
         stage_rows_b<HD, BC, NW>(make_rsrc(V + head + (size_t)k0 * HD, bytes), vo_k, smem + S::off_v, w);
     }
@@ -460,6 +460,355 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 }
 
 // ----------------------------------------------------------------------------
+// Kernel A for d = 128, one wave per SIMD: one workgroup of 4 wave64s per
+// (batch*head, 256-key tile); wave w owns keys 64 w .. + 63 (two 32-key blocks
+// kb) and all 64 rows of each query tile, so every Q_i / dO_i operand read from
+// LDS feeds two MFMAs (one per key block) and no dK / dV partials need
+// combining.  K_j stays in VGPRs as the B operand of S = Q K^T; V_j sits in
+// LDS; the dK / dV accumulators (64 keys x 128 columns each) take the
+// accumulation registers.  The two 32-row halves qb of a query tile are
+// processed one after the other.  dS^T tiles and the K image are written in
+// the 128-key format the dQ kernel reads.
+// ----------------------------------------------------------------------------
+constexpr int BC2 = 256;                         // keys per workgroup
+constexpr int NW2 = 4;
+
+struct Smem2 {
+    static constexpr int HD = 128;
+    static constexpr int TILE = BR * HD * 2;              // one Q_i or dO_i buffer (16 KiB)
+    static constexpr int off_q = 0;                       // two buffers
+    static constexpr int off_do = 2 * TILE;               // two buffers
+    static constexpr int off_v = 4 * TILE;                // V_j, 256 x 128
+    static constexpr int off_l = off_v + BC2 * HD * 2;    // float[2][BR]
+    static constexpr int off_d = off_l + 2 * BR * 4;      // float[2][BR]
+    static constexpr int bytes = off_d + 2 * BR * 4;
+    static constexpr int off_kstage = 0;                  // K_j in the prologue (overlays Q/dO)
+    static_assert(BC2 * HD * 2 <= off_v, "K staging must fit below V");
+};
+
+// The S / dP products of this kernel are issued as VGPR-form MFMAs: with the
+// 256 dK / dV accumulator registers in the AGPR file, leaving the choice to the
+// compiler puts every MFMA result in AGPRs and overflows them.  Hazards this
+// implies (the compiler inserts them for its own MFMAs): a VALU read of an
+// MFMA result needs 12 wait states after the MFMA (mfma_v_settle gives 16),
+// dependent accumulation and LDS loads into the operand registers need none.
+__device__ __forceinline__ void mfma_v(f32x16& c, const bf16x8& a, const bf16x8& b) {
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+}
+
+__device__ __forceinline__ void mfma_v0(f32x16& c, const bf16x8& a, const bf16x8& b) {
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(c) : "v"(a), "v"(b));
+}
+
+__device__ __forceinline__ void mfma_v_settle(f32x16& a, f32x16& b, f32x16& c, f32x16& d) {
+    asm volatile("s_nop 15" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+}
+
+// Transposing LDS reads issued from inline assembly.  The compiler treats its
+// own ds_read_b64_tr_b16 as possibly reading what an in-flight buffer -> LDS
+// copy writes and waits for all of them (vmcnt(0)) first, which would expose
+// the next tile's copy latency in every iteration; these reads only touch the
+// current tile, which the copies never write.  The compiler does not track
+// their completion, so tr_wait must follow before the results are used: with
+// `pending` = the number of LDS reads issued after them, lgkmcnt(pending)
+// guarantees they are done (LDS operations complete in order).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p);
+}
+
+__device__ __forceinline__ void tr_read4(u32x2& a, u32x2& b, u32x2& c, u32x2& d, uint32_t pa,
+                                         uint32_t pb, uint32_t pc, uint32_t pd) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %4\n\t"
+        "ds_read_b64_tr_b16 %1, %5\n\t"
+        "ds_read_b64_tr_b16 %2, %6\n\t"
+        "ds_read_b64_tr_b16 %3, %7"
+        : "=&v"(a), "=&v"(b), "=&v"(c), "=&v"(d)
+        : "v"(pa), "v"(pb), "v"(pc), "v"(pd));
+}
+
+template <int PENDING>
+__device__ __forceinline__ void tr_wait(u32x2& a, u32x2& b, u32x2& c, u32x2& d) {
+    static_assert(PENDING == 0 || PENDING == 4, "pending count");
+    if (PENDING == 0)
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+    else
+        asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+}
+
+__device__ __forceinline__ bf16x8 cat_u(u32x2 lo, u32x2 hi) {
+    return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+}
+
+template <bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW2 * 64, NW2 * 64), amdgpu_waves_per_eu(1, 1)))
+void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+                         const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
+                         const float* __restrict__ Lb, const float* __restrict__ Dp,
+                         __bf16* __restrict__ dSw, __bf16* __restrict__ Kimg,
+                         __bf16* __restrict__ dK, __bf16* __restrict__ dV, int BH, int N,
+                         int n_pad, float scale) {
+    constexpr int HD = 128;
+    using S = Smem2;
+    constexpr int KSD = HD / 16;                 // 8 k steps over the head dim
+    constexpr int DB = HD / 32;                  // 4 column blocks
+    constexpr int TILE_EL = BR * HD;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+
+    const int lane = threadIdx.x & 63;
+    const int w = wave_id();
+    const int l32 = lane & 31;
+    const int g = lane >> 5;
+    const int t16 = lane & 15;
+    const int hh = (lane >> 4) & 1;
+    const int s4 = t16 >> 2;
+
+    const int tc2 = (N + BC2 - 1) / BC2;
+    const int tc = (N + BC - 1) / BC;            // 128-key tiles (dS^T and K image format)
+    const int tr_count = (N + BR - 1) / BR;
+    // causal: key tile j has (N - 256 j) / 64 query tiles, so dispatch all
+    // heads' tile 0 first, then tile 1, ... (longest first); workgroups are
+    // dealt round-robin over the 8 XCDs, so when B*H is a multiple of 8 every
+    // tile of a head still runs on the same XCD.  Non-causal tiles are equal;
+    // consecutive tiles of a head go to the same XCD.
+    int bh, j;
+    if (CAUSAL) {
+        bh = blockIdx.x % BH;
+        j = blockIdx.x / BH;
+    } else {
+        const int logical = xcd_remap(blockIdx.x, BH * tc2);
+        bh = logical / tc2;
+        j = logical % tc2;
+    }
+    const int k0 = j * BC2;
+    const int kw0 = k0 + 64 * w;                 // this wave's first key
+
+    const size_t head = (size_t)bh * N * HD;
+    const __bf16* Qh = Q + head;
+    const __bf16* dOh = dO + head;
+    const float* Lbh = Lb + (size_t)bh * n_pad;
+    const float* Dph = Dp + (size_t)bh * n_pad;
+    const __bf16* VS = reinterpret_cast<const __bf16*>(smem + S::off_v);
+    const __bf16* KS = reinterpret_cast<const __bf16*>(smem + S::off_kstage);
+
+    // row reads: chunk 2 i + g of row l32 (+ a multiple of 16 rows keeps the
+    // swizzle); k steps 4..7 flip chunk bit 3 (offset ^ 64)
+    // (2 ks + g) ^ swz = ((g ^ swz) & 1 | (swz & ~1) ^ 2 ks): offset ob0 ^ 16 ks
+    const int ob0 = roff<HD>(l32, g);
+    // transposing reads of dO_i / Q_i: rows 4 g + s4 (+ 16 k4, + 32 qb, + 8),
+    // columns 16 hh + 4 (t16 & 3) (+ 32 db)
+    const int otr = roff4<HD>(g * 4 + s4, hh * 16 + 4 * (t16 & 3));
+    const int it0 = CAUSAL ? (k0 / BR) : 0;
+
+    // ---- K_j, V_j into LDS; then K_j into registers and the K image
+    constexpr int ROWB = HD * 2;
+    int vo_q[BR * (HD / 8) / 64 / NW2], vo_k[BC2 * (HD / 8) / 64 / NW2];
+    stage_offsets<HD, BR, NW2>(vo_q, w, lane);
+    stage_offsets<HD, BC2, NW2>(vo_k, w, lane);
+    {
+        const int rows = min(N - k0, BC2);
+        stage_rows_b<HD, BC2, NW2>(make_rsrc(K + head + (size_t)k0 * HD, rows * ROWB), vo_k,
+                                   smem + S::off_kstage, w);
+        stage_rows_b<HD, BC2, NW2>(make_rsrc(V + head + (size_t)k0 * HD, rows * ROWB), vo_k,
+                                   smem + S::off_v, w);
+    }
+    __syncthreads();
+    bf16x8 kreg[2][KSD];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks)
+            kreg[kb][ks] = lds_read16(KS + (ob0 ^ (ks * 16)) + (64 * w + 32 * kb) * HD);
+    {
+        // 128-key image tile jt = w >> 1 of this workgroup; 32 blocks of 1 KiB,
+        // 16 per wave
+        const int jt = w >> 1, jg = 2 * j + jt;
+        if (jg < tc) {
+            const __amdgpu_buffer_rsrc_t kr = make_rsrc(Kimg + kimg_tile(bh, jg, tc, HD), BC * HD * 2);
+#pragma unroll
+            for (int b = 0; b < 16; ++b) {
+                const int blk = (w & 1) * 16 + b;
+                const int bdb = blk / (BC / 16), bks = blk % (BC / 16);
+                const int key = jt * BC + bks * 16 + g * 8 + s4;
+                const int col = bdb * 32 + hh * 16 + 4 * (t16 & 3);
+                const bf16x8 v = cat44(lds_read_tr(KS + roff4<HD>(key, col)),
+                                       lds_read_tr(KS + roff4<HD>(key + 4, col)));
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), kr,
+                                                       (blk * 64 + lane) * 16, 0, 0);
+            }
+        }
+    }
+    __syncthreads();                             // K staging consumed
+
+    auto stage_tile = [&](int it, int buf) {
+        const int q0 = it * BR;
+        const int bytes = min(N - q0, BR) * ROWB;
+        stage_rows_b<HD, BR, NW2>(make_rsrc(Qh + (size_t)q0 * HD, bytes), vo_q,
+                                  smem + S::off_q + buf * S::TILE, w);
+        stage_rows_b<HD, BR, NW2>(make_rsrc(dOh + (size_t)q0 * HD, bytes), vo_q,
+                                  smem + S::off_do + buf * S::TILE, w);
+        if (w == 0) bdma4(make_rsrc(Lbh + q0, BR * 4), lane * 4, smem + S::off_l + buf * BR * 4);
+        if (w == 1) bdma4(make_rsrc(Dph + q0, BR * 4), lane * 4, smem + S::off_d + buf * BR * 4);
+    };
+    stage_tile(it0, 0);
+    __syncthreads();
+
+    f32x16 dv[2][DB], dk[2][DB];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int b = 0; b < DB; ++b) {
+            dv[kb][b] = zero16();
+            dk[kb][b] = zero16();
+        }
+    const float sl2 = scale * kLog2e;
+    // dS^T stores: key row (w & 1) * 64 + 32 kb + l32 of 128-key tile 2 j + (w >> 1),
+    // units 8 qb + 2 rr + g (qb = 1 flips unit bit 3: offset ^ 32)
+    // unit 2 rr + g: offset ow0 ^ 8 rr
+    const int ow0 = toff((w & 1) * 64 + l32, g);
+    const int jst = 2 * j + (w >> 1);
+
+    for (int it = it0, buf = 0; it < tr_count; ++it, buf ^= 1) {
+        const int q0 = it * BR;
+        if (it + 1 < tr_count) stage_tile(it + 1, buf ^ 1);     // lands during this iteration
+        const __bf16* Qs = reinterpret_cast<const __bf16*>(smem + S::off_q) + buf * TILE_EL;
+        const __bf16* dOs = reinterpret_cast<const __bf16*>(smem + S::off_do) + buf * TILE_EL;
+        const float* Ls = reinterpret_cast<const float*>(smem + S::off_l) + buf * BR;
+        const float* Ds = reinterpret_cast<const float*>(smem + S::off_d) + buf * BR;
+        const __amdgpu_buffer_rsrc_t dsr =
+            make_rsrc(dSw + dst_tile(bh, it, min(jst, tc - 1), tr_count, tc), DST_EL * 2);
+
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            // ---- S = Q K^T, dP = dO V^T: 32 queries x 64 keys (two key blocks)
+            f32x16 s[2], dp[2];
+#pragma unroll
+            for (int ks = 0; ks < KSD; ++ks) {
+                const int oa = (ob0 ^ (ks * 16)) + qb * 32 * HD;
+                const bf16x8 aq = lds_read16(Qs + oa);
+                const bf16x8 ado = lds_read16(dOs + oa);
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    const bf16x8 bv = lds_read16(VS + (ob0 ^ (ks * 16)) + (64 * w + 32 * kb) * HD);
+                    if (ks == 0) {
+                        mfma_v0(s[kb], aq, kreg[kb][ks]);
+                        mfma_v0(dp[kb], ado, bv);
+                    } else {
+                        mfma_v(s[kb], aq, kreg[kb][ks]);
+                        mfma_v(dp[kb], ado, bv);
+                    }
+                }
+            }
+            mfma_v_settle(s[0], s[1], dp[0], dp[1]);
+            __builtin_amdgcn_sched_barrier(0);
+            // ---- masking where this block's keys reach past its first query
+            //      row (causal diagonal) or past the end
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const int kb0 = kw0 + 32 * kb;
+                const bool need_mask = (kb0 + 32 > N) || (CAUSAL && (kb0 + 31 > q0 + 32 * qb));
+                if (__builtin_expect(need_mask, 0)) {
+                    const int key = kb0 + l32;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int q = q0 + 32 * qb + (r >> 2) * 8 + g * 4 + (r & 3);
+                        const bool masked = (key >= N) || (CAUSAL && key > q);
+                        s[kb][r] = masked ? -__builtin_inff() : s[kb][r];
+                    }
+                }
+            }
+            // ---- P = exp(scale S - L), dS = P o (dP - D)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const f32x4 lv = *reinterpret_cast<const f32x4*>(Ls + 32 * qb + g * 4 + rr * 8);
+                const f32x4 dd = *reinterpret_cast<const f32x4*>(Ds + 32 * qb + g * 4 + rr * 8);
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = rr * 4 + e;
+                        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], sl2, -lv[e]));
+                        s[kb][r] = p;
+                        dp[kb][r] = p * (dp[kb][r] - dd[e]);
+                    }
+            }
+            bf16x8 pa[2][2], da[2][2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                pa[kb][0] = pack_c8(s[kb], 0);
+                pa[kb][1] = pack_c8(s[kb], 8);
+                da[kb][0] = pack_c8(dp[kb], 0);
+                da[kb][1] = pack_c8(dp[kb], 8);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            // ---- dS^T for the dQ kernel
+            if (jst < tc) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    const u32x4 d0 = __builtin_bit_cast(u32x4, da[kb][0]);
+                    const u32x4 d1 = __builtin_bit_cast(u32x4, da[kb][1]);
+                    const int kro = kb * 32 * BR;
+                    __builtin_amdgcn_raw_buffer_store_b64(u32x2{d0[0], d0[1]}, dsr, (((ow0 ^ (0 * 8)) + kro) ^ (qb * 32)) * 2, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b64(u32x2{d0[2], d0[3]}, dsr, (((ow0 ^ (1 * 8)) + kro) ^ (qb * 32)) * 2, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b64(u32x2{d1[0], d1[1]}, dsr, (((ow0 ^ (2 * 8)) + kro) ^ (qb * 32)) * 2, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b64(u32x2{d1[2], d1[3]}, dsr, (((ow0 ^ (3 * 8)) + kro) ^ (qb * 32)) * 2, 0, 0);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            // ---- dV += P^T dO, dK += dS^T Q over these 32 queries; the B
+            //      operand of each (db, k4) feeds both key blocks
+            {
+                const uint32_t aq = lds_addr(Qs), ado = lds_addr(dOs);
+                auto addr = [&](int step, uint32_t base, int half) -> uint32_t {
+                    const int db = step >> 1, k4 = step & 1;
+                    const int o = half ? (((otr + 8 * HD) ^ (db << 5) ^ 16)) : (otr ^ (db << 5));
+                    return base + (uint32_t)((o + qb * 32 * HD + k4 * 16 * HD) * 2);
+                };
+                u32x2 c0, c1, c2, c3, n0, n1, n2, n3;
+                tr_read4(c0, c1, c2, c3, addr(0, ado, 0), addr(0, ado, 1), addr(0, aq, 0), addr(0, aq, 1));
+#pragma unroll
+                for (int step = 0; step < 2 * DB; ++step) {
+                    const int db = step >> 1, k4 = step & 1;
+                    if (step + 1 < 2 * DB) {
+                        tr_read4(n0, n1, n2, n3, addr(step + 1, ado, 0), addr(step + 1, ado, 1),
+                                 addr(step + 1, aq, 0), addr(step + 1, aq, 1));
+                        tr_wait<4>(c0, c1, c2, c3);
+                    } else {
+                        tr_wait<0>(c0, c1, c2, c3);
+                    }
+                    const bf16x8 bo = cat_u(c0, c1), bq = cat_u(c2, c3);
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb) {
+                        dv[kb][db] = mfma32(pa[kb][k4], bo, dv[kb][db]);
+                        dk[kb][db] = mfma32(da[kb][k4], bq, dk[kb][db]);
+                    }
+                    c0 = n0;
+                    c1 = n1;
+                    c2 = n2;
+                    c3 = n3;
+                }
+            }
+        }
+        __syncthreads();                         // next tile landed; this one free
+    }
+
+    // ---- epilogue: dV, dK (scaled) of this wave's 64 keys
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = kw0 + 32 * kb + (r >> 2) * 8 + g * 4 + (r & 3);
+                if (key < N) {
+                    const size_t off = head + (size_t)key * HD + db * 32 + l32;
+                    dV[off] = (__bf16)dv[kb][db][r];
+                    dK[off] = (__bf16)(dk[kb][db][r] * scale);
+                }
+            }
+}
+
+// ----------------------------------------------------------------------------
 // Kernel B: dQ_i = scale * sum_j dS_ij K_j, one workgroup of 4 wave64s per
 // (batch*head, 64-row query tile i).  The dS^T tiles written by kernel A are
 // copied into an LDS double buffer one step ahead and read transposed (A
@@ -480,7 +829,7 @@ void bwd_dq_kernel(const __bf16* __restrict__ Kimg, const __bf16* __restrict__ d
     __shared__ __attribute__((aligned(16))) char smem[2 * DS_B];
 
     const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
+    const int w = wave_id();
     const int db = w % DB;                       // this wave's 32 head-dim columns
     const int qb0 = (TQ == 2) ? 0 : (w / DB);    // its first 32-row query block
     const int g = lane >> 5;
@@ -613,6 +962,20 @@ template <int HD, bool CAUSAL>
 static hipError_t launch_dkdv(const void* q, const void* k, const void* v, const void* dO,
                               const float* Lb, const float* Dp, __bf16* dSw, __bf16* kimg, void* dk,
                               void* dv, int BH, int N, int n_pad, float scale, hipStream_t stream) {
+#ifndef ATTN_DKDV_W32
+    if (HD == 128) {
+        using S2 = bwd::Smem2;
+        auto kern = bwd::bwd_dkdv_w64_kernel<CAUSAL>;
+        hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, S2::bytes);
+        if (e != hipSuccess) return e;
+        const int tc2 = (N + bwd::BC2 - 1) / bwd::BC2;
+        hipLaunchKernelGGL(kern, dim3(BH * tc2), dim3(bwd::NW2 * 64), S2::bytes, stream,
+                           (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dO,
+                           Lb, Dp, dSw, kimg, (__bf16*)dk, (__bf16*)dv, BH, N, n_pad, scale);
+        return hipGetLastError();
+    }
+#endif
     using S = bwd::Smem<HD>;
     auto kern = bwd::bwd_dkdv_kernel<HD, CAUSAL>;
     hipError_t e = hipFuncSetAttribute((const void*)kern,

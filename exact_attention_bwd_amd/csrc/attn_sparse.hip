@@ -121,7 +121,7 @@ void sfwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                  int Hq, int Nq, int Nkv, int topk, float scale) {
     using S = FwdSmem;
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, w = wave_id();
     const int hb = w & 1, vh = w >> 1, pw = w ^ 2;   // partner: same heads, other half
     const int l32 = lane & 31, g = lane >> 5, t16 = lane & 15, hh = (lane >> 4) & 1, s4 = t16 >> 2;
     const int G = Hq / HG;
@@ -281,7 +281,7 @@ void sbwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
                       int topk, int tpad, float scale) {
     using S = BwdSmem;
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, w = wave_id();
     const int l32 = lane & 31, g = lane >> 5, t16 = lane & 15, hh = (lane >> 4) & 1, s4 = t16 >> 2;
     const int G = Hq / HG;
     const int logical = xcd_remap(blockIdx.x, Nq * G);
@@ -456,7 +456,7 @@ void sbwd_dq_kernel(const __bf16* __restrict__ K, const __bf16* __restrict__ dsw
                     __bf16* __restrict__ dQ, int Hq, int Nq, int Nkv, int topk, int tpad,
                     float scale) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, w = wave_id();
     const int l32 = lane & 31, g = lane >> 5, t16 = lane & 15, hh = (lane >> 4) & 1, s4 = t16 >> 2;
     const int hb = w & 1, db0 = (w >> 1) * 9;
     const int G = Hq / HG;

@@ -127,6 +127,12 @@ __device__ __forceinline__ void bdma4(__amdgpu_buffer_rsrc_t r, int voff, void* 
                                              voff, 0, 0, 0);
 }
 
+// Index of this lane's wave in the workgroup, as a wave-uniform (scalar) value:
+// values derived from it (LDS bases, buffer descriptors) stay in SGPRs.
+__device__ __forceinline__ int wave_id() {
+    return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+}
+
 __device__ __forceinline__ float wave_max_pair32(float x) {
     // combine lane l with lane l ^ 32
     return fmaxf(x, __shfl_xor(x, 32));
