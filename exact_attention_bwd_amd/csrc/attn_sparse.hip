@@ -41,6 +41,8 @@ constexpr int VROW = 1024;             // LDS row stride (bytes) of a 512-wide b
 constexpr int PW = DV + DQK;           // fp32 words of one (row, slot) dK/dV contribution
 constexpr int RB = 64;                 // query rows per block of the index transpose
 constexpr int MAX_NKV = 16384;         // keys the transpose can count in LDS
+constexpr int SBW_WAVES = 8;           // waves of the per-row backward kernel
+constexpr int SBW_CHUNK = SBW_WAVES * 32;   // slots per chunk of that kernel
 
 // LDS rows start on a 256-byte bank line; the 16-byte chunk c of row r is
 // stored at chunk (c & ~15) | ((c & 15) ^ lswz(r)).  For any 16 consecutive
@@ -258,8 +260,9 @@ void sfwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 // ----------------------------------------------------------------------------
 // Backward, per (query row, head group): recompute S = Q_i K_I^T, P, dP =
 // dO_i V_I^T and dS; store dS (bf16) for the dQ kernel and each slot's dV and
-// (unscaled) dK contribution, summed over the 64 heads, as fp32.  Wave w owns
-// slots 32 w .. + 31 of every 128-slot chunk and all 64 heads: S and dP have
+// (unscaled) dK contribution, summed over the 64 heads, as fp32.  Eight waves
+// (two per SIMD); wave w owns slots 32 w .. + 31 of every 256-slot chunk and
+// all 64 heads: S and dP have
 // one slot per lane, which is the A layout of P^T and dS^T for dV = P^T dO and
 // dK = dS^T Q (k = heads); dO_i and Q_i sit in LDS for the whole row and are
 // read row-wise (A operands of S, dP) and transposed (B operands of dV, dK).
@@ -272,7 +275,7 @@ struct BwdSmem {
     static constexpr int bytes = off_d + HG * 4;
 };
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void sbwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                       const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                       const float* __restrict__ Lse, const float* __restrict__ Dd,
@@ -287,14 +290,14 @@ void sbwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
     const int logical = xcd_remap(blockIdx.x, Nq * G);
     const int i = logical / G, hg = logical % G;
     const int nval = valid_slots(tlen, i, topk);
-    const int nchunks = (nval + 127) / 128;
+    const int nchunks = (nval + SBW_CHUNK - 1) / SBW_CHUNK;
     const int* irow = idx + (size_t)i * topk;
     const size_t rowg = (size_t)i * G + hg;      // (row, head group) index
 
-    // ---- Q_i, dO_i of the 64 heads into LDS (rows 16 w .. + 15 per wave); L, D
+    // ---- Q_i, dO_i of the 64 heads into LDS (rows 8 w .. + 7 per wave); L, D
 #pragma unroll 4
-    for (int rr = 0; rr < 16; ++rr) {
-        const int h = w * 16 + rr;
+    for (int rr = 0; rr < 8; ++rr) {
+        const int h = w * 8 + rr;
         const size_t hrow = (size_t)(hg * HG + h) * Nq + i;
         stage_qrow(make_rsrc(Q + hrow * DQK, DQK * 2), 0, smem + S::off_q, h, lane);
         stage_vrow(make_rsrc(dO + hrow * DV, DV * 2), 0, smem + S::off_do, h, lane);
@@ -319,7 +322,7 @@ void sbwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
     (void)dOs;
 
     for (int c = 0; c < nchunks; ++c) {
-        const int slot = c * 128 + w * 32 + l32;                  // this lane's slot
+        const int slot = c * SBW_CHUNK + w * 32 + l32;            // this lane's slot
         const int key = slot_key(irow, slot, nval, Nkv);
         const uint64_t vmask = __ballot(key >= 0);               // bit l32 (g = 0 half)
         const int kbq = (key < 0 ? Nkv : key) * (DQK * 2) + 16 * g;
@@ -332,27 +335,45 @@ void sbwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
             sc[hb] = zero16();
             dp[hb] = zero16();
         }
+        // gathered K / V operands in groups of 4 k steps, one group in flight
+        // ahead of the products (the sched barriers keep the compiler from
+        // hoisting all 68 loads)
+        constexpr int GK = 4;
+        auto gload = [&](__amdgpu_buffer_rsrc_t rs, int base, int ks) {
+            return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, base + 32 * ks, 0, 0));
+        };
+        bf16x8 gcur[GK], gnext[GK];
 #pragma unroll
-        for (int ks = 0; ks < DQK / 16; ++ks) {
-            const bf16x8 b = __builtin_bit_cast(
-                bf16x8, __builtin_amdgcn_raw_buffer_load_b128(krs, kbq + 32 * ks, 0, 0));
+        for (int e = 0; e < GK; ++e) gcur[e] = gload(krs, kbq, e);
 #pragma unroll
-            for (int hb = 0; hb < 2; ++hb) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                    Qb + loff<QROW>(hb * 32 + l32, 16 * ks + 8 * g));
-                sc[hb] = mfma32(a, b, sc[hb]);
+        for (int grp = 0; grp < (DQK + DV) / 16 / GK; ++grp) {
+            const int ks0 = grp * GK;                              // 0..35 K, 36..67 V
+            if (grp + 1 < (DQK + DV) / 16 / GK) {
+#pragma unroll
+                for (int e = 0; e < GK; ++e) {
+                    const int ks = ks0 + GK + e;
+                    gnext[e] = ks < DQK / 16 ? gload(krs, kbq, ks) : gload(vrs, kbv, ks - DQK / 16);
+                }
             }
-        }
 #pragma unroll
-        for (int ks = 0; ks < DV / 16; ++ks) {
-            const bf16x8 b = __builtin_bit_cast(
-                bf16x8, __builtin_amdgcn_raw_buffer_load_b128(vrs, kbv + 32 * ks, 0, 0));
+            for (int e = 0; e < GK; ++e) {
+                const int ks = ks0 + e;
 #pragma unroll
-            for (int hb = 0; hb < 2; ++hb) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                    dOb + loff<VROW>(hb * 32 + l32, 16 * ks + 8 * g));
-                dp[hb] = mfma32(a, b, dp[hb]);
+                for (int hb = 0; hb < 2; ++hb) {
+                    if (ks < DQK / 16) {
+                        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                            Qb + loff<QROW>(hb * 32 + l32, 16 * ks + 8 * g));
+                        sc[hb] = mfma32(a, gcur[e], sc[hb]);
+                    } else {
+                        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                            dOb + loff<VROW>(hb * 32 + l32, 16 * (ks - DQK / 16) + 8 * g));
+                        dp[hb] = mfma32(a, gcur[e], dp[hb]);
+                    }
+                }
             }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int e = 0; e < GK; ++e) gcur[e] = gnext[e];
         }
         // ---- P = exp(scale S - L) (0 for absent slots), dS = P (dP - D)
         const bool live = key >= 0;
@@ -396,18 +417,18 @@ void sbwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
         // ---- dV and dK contributions of the 32 slots, 4 column blocks at a time:
         //      C[m = slot][n = column], k = the 64 heads
         float* prow = part + (rowg * topk) * PW;
-        const int slot0 = c * 128 + w * 32;
+        const int slot0 = c * SBW_CHUNK + w * 32;
         auto contrib = [&](const char* tile, int stride, bool is_v, int nblk, int blk0, int colbase) {
-            f32x16 cacc[4];
+            f32x16 cacc[2];
 #pragma unroll
-            for (int b = 0; b < 4; ++b) cacc[b] = zero16();
+            for (int b = 0; b < 2; ++b) cacc[b] = zero16();
 #pragma unroll
             for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
                 for (int k4 = 0; k4 < 2; ++k4) {
                     const int hr = hb * 32 + 16 * k4 + 4 * g + s4;
 #pragma unroll
-                    for (int b = 0; b < 4; ++b) {
+                    for (int b = 0; b < 2; ++b) {
                         if (b < nblk) {
                             const int col = 32 * (blk0 + b) + 16 * hh + 4 * (t16 & 3);
                             const int o0 = stride == QROW ? loff<QROW>(hr, col) : loff<VROW>(hr, col);
@@ -419,7 +440,7 @@ void sbwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
                     }
                 }
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
+            for (int b = 0; b < 2; ++b) {
                 if (b < nblk) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
@@ -431,10 +452,9 @@ void sbwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
             }
         };
 #pragma unroll 1
-        for (int blk = 0; blk < DV / 32; blk += 4) contrib(dOb, VROW, true, 4, blk, 0);
+        for (int blk = 0; blk < DV / 32; blk += 2) contrib(dOb, VROW, true, 2, blk, 0);
 #pragma unroll 1
-        for (int blk = 0; blk < DQK / 32; blk += 4)
-            contrib(Qb, QROW, false, (DQK / 32 - blk) < 4 ? (DQK / 32 - blk) : 4, blk, DV);
+        for (int blk = 0; blk < DQK / 32; blk += 2) contrib(Qb, QROW, false, 2, blk, DV);
     }
 }
 
@@ -614,39 +634,67 @@ __global__ __launch_bounds__(256) void sidx_fill_kernel(const int* __restrict__ 
 
 // Per key: dV_j = sum over its (row, slot) pairs and head groups of the stored
 // contributions, dK_j = scale * the same sum of the dK parts; one wave per key,
-// lane l sums words l, l + 64, ... of the 1088-word contribution rows.
+// in the fixed list order.  Lane l sums the 16-byte chunks l, l + 64, l + 128,
+// l + 192 of each 4352-byte contribution row and word 1024 + l; rows are
+// loaded four at a time so that 20 loads per lane are in flight.
 __global__ __launch_bounds__(256) void sbwd_reduce_kernel(const float* __restrict__ part,
                                                           const int* __restrict__ off,
                                                           const int* __restrict__ list,
                                                           __bf16* __restrict__ dK,
                                                           __bf16* __restrict__ dV, int Nkv, int G,
                                                           int topk, float scale) {
-    constexpr int NW = (PW + 63) / 64;           // 17 words per lane
+    static_assert(PW == 4 * 256 + 64, "row layout: four 1 KiB chunks per 64 lanes and 64 words");
     const int lane = threadIdx.x & 63;
-    const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int j = blockIdx.x * 4 + wave_id();
     if (j >= Nkv) return;
-    float acc[NW];
+    f32x4 acc[4];
+    float acct = 0.f;
 #pragma unroll
-    for (int c = 0; c < NW; ++c) acc[c] = 0.f;
-    const int e0 = off[j], e1 = off[j + 1];
-    for (int e = e0; e < e1; ++e) {
-        const int pr = list[e];                   // i * topk + s
+    for (int c = 0; c < 4; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // contribution rows of key j: (list entry e, head group hg), e in list order
+    const int e0 = off[j];
+    const int nrows = (off[j + 1] - e0) * G;
+    auto row_of = [&](int r) -> const float* {
+        const int pr = list[e0 + r / G];          // i * topk + s
         const int i = pr / topk, s = pr - i * topk;
-        for (int hg = 0; hg < G; ++hg) {
-            const float* row = part + (((size_t)i * G + hg) * topk + s) * PW;
+        return part + (((size_t)i * G + r % G) * topk + s) * PW;
+    };
+    int r = 0;
+    for (; r + 4 <= nrows; r += 4) {
+        f32x4 v[4][4];
+        float t[4];
 #pragma unroll
-            for (int c = 0; c < NW; ++c) {
-                const int col = c * 64 + lane;
-                if (col < PW) acc[c] += row[col];
-            }
+        for (int u = 0; u < 4; ++u) {
+            const float* row = row_of(r + u);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) v[u][c] = reinterpret_cast<const f32x4*>(row)[c * 64 + lane];
+            t[u] = row[1024 + lane];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[c] += v[u][c];
+            acct += t[u];
         }
     }
+    for (; r < nrows; ++r) {
+        const float* row = row_of(r);
 #pragma unroll
-    for (int c = 0; c < NW; ++c) {
-        const int col = c * 64 + lane;
-        if (col < DV) dV[(size_t)j * DV + col] = (__bf16)acc[c];
-        else if (col < PW) dK[(size_t)j * DQK + col - DV] = (__bf16)(acc[c] * scale);
+        for (int c = 0; c < 4; ++c) acc[c] += reinterpret_cast<const f32x4*>(row)[c * 64 + lane];
+        acct += row[1024 + lane];
     }
+    // columns 4 lane + 256 c (+0..3): c = 0, 1 are dV, c = 2, 3 and 1024 + lane are dK
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int col = 4 * lane + 256 * c;
+        if (c < 2) {
+            *reinterpret_cast<bf16x4*>(dV + (size_t)j * DV + col) = __builtin_convertvector(acc[c], bf16x4);
+        } else {
+            *reinterpret_cast<bf16x4*>(dK + (size_t)j * DQK + col - DV) =
+                __builtin_convertvector(acc[c] * scale, bf16x4);
+        }
+    }
+    dK[(size_t)j * DQK + 1024 + lane - DV] = (__bf16)(acct * scale);
 }
 
 }  // namespace sp
@@ -654,7 +702,7 @@ __global__ __launch_bounds__(256) void sbwd_reduce_kernel(const float* __restric
 // ----------------------------------------------------------------------------
 // Host launchers
 // ----------------------------------------------------------------------------
-static int sp_tpad(int topk) { return ((topk + 127) / 128) * 128; }
+static int sp_tpad(int topk) { return ((topk + sp::SBW_CHUNK - 1) / sp::SBW_CHUNK) * sp::SBW_CHUNK; }
 
 static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -728,7 +776,7 @@ hipError_t launch_sparse_bwd(const void* q, const void* k, const void* v, const 
                                      hipFuncAttributeMaxDynamicSharedMemorySize, smem_dq)) != hipSuccess)
             return e;
         if (main_start && (e = hipEventRecord(main_start, stream)) != hipSuccess) return e;
-        hipLaunchKernelGGL(sp::sbwd_main_kernel, dim3(Nq * G), dim3(256), smem_main, stream,
+        hipLaunchKernelGGL(sp::sbwd_main_kernel, dim3(Nq * G), dim3(sp::SBW_WAVES * 64), smem_main, stream,
                            (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dO,
                            lse, D, idx, tlen, dsw, part, Hq, Nq, Nkv, topk, tpad, scale);
         if ((e = hipGetLastError()) != hipSuccess) return e;
