@@ -39,7 +39,7 @@ constexpr int HG = 64;                 // query heads per workgroup
 constexpr int QROW = 1280;             // LDS row stride (bytes) of a 576-wide bf16 row
 constexpr int VROW = 1024;             // LDS row stride (bytes) of a 512-wide bf16 row
 constexpr int PW = DV + DQK;           // fp32 words of one (row, slot) dK/dV contribution
-constexpr int RB = 64;                 // query rows per block of the index transpose
+constexpr int RB = 16;                 // query rows per block of the index transpose
 constexpr int MAX_NKV = 16384;         // keys the transpose can count in LDS
 constexpr int SBW_WAVES = 8;           // waves of the per-row backward kernel
 constexpr int SBW_CHUNK = SBW_WAVES * 32;   // slots per chunk of that kernel
@@ -568,25 +568,40 @@ __global__ __launch_bounds__(256) void sidx_hist_kernel(const int* __restrict__ 
     for (int j = threadIdx.x; j < Nkv; j += 256) cnt[(size_t)b * Nkv + j] = h[j];
 }
 
-// One workgroup: per key, the exclusive running count over row blocks (in
-// place), then the exclusive scan of the per-key totals into off[0..Nkv].
-__global__ __launch_bounds__(1024) void sidx_scan_kernel(int* __restrict__ cnt, int* __restrict__ off,
-                                                         int nb, int Nkv) {
+// Per key (one thread each): the exclusive running count over row blocks, in
+// place, and the key's total into off[j].
+__global__ __launch_bounds__(64) void sidx_colscan_kernel(int* __restrict__ cnt, int* __restrict__ off,
+                                                          int nb, int Nkv) {
+    const int j = blockIdx.x * 64 + threadIdx.x;
+    if (j >= Nkv) return;
+    int run = 0;
+    int b = 0;
+    for (; b + 8 <= nb; b += 8) {                 // eight independent loads in flight
+        int c[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) c[u] = cnt[(size_t)(b + u) * Nkv + j];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            cnt[(size_t)(b + u) * Nkv + j] = run;
+            run += c[u];
+        }
+    }
+    for (; b < nb; ++b) {
+        const int c = cnt[(size_t)b * Nkv + j];
+        cnt[(size_t)b * Nkv + j] = run;
+        run += c;
+    }
+    off[j] = run;
+}
+
+// One workgroup: exclusive scan of the per-key totals into off[0..Nkv].
+__global__ __launch_bounds__(1024) void sidx_keyscan_kernel(int* __restrict__ off, int Nkv) {
     __shared__ int part[1024];
     const int t = threadIdx.x;
     const int per = (Nkv + 1023) / 1024;
     const int j0 = t * per, j1 = min(Nkv, j0 + per);
     int run_total = 0;
-    for (int j = j0; j < j1; ++j) {
-        int run = 0;
-        for (int b = 0; b < nb; ++b) {
-            const int c = cnt[(size_t)b * Nkv + j];
-            cnt[(size_t)b * Nkv + j] = run;
-            run += c;
-        }
-        off[j] = run;                             // total for now
-        run_total += run;
-    }
+    for (int j = j0; j < j1; ++j) run_total += off[j];
     part[t] = run_total;
     __syncthreads();
     for (int d = 1; d < 1024; d <<= 1) {          // inclusive scan of the partials
@@ -759,7 +774,12 @@ hipError_t launch_sparse_bwd(const void* q, const void* k, const void* v, const 
                            Nkv, topk);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(sp::sidx_scan_kernel, dim3(1), dim3(1024), 0, stream, cnt, off, nb, Nkv);
+    if (Nkv > 0) {
+        hipLaunchKernelGGL(sp::sidx_colscan_kernel, dim3((Nkv + 63) / 64), dim3(64), 0, stream, cnt,
+                           off, nb, Nkv);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(sp::sidx_keyscan_kernel, dim3(1), dim3(1024), 0, stream, off, Nkv);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (nb > 0) {
         hipLaunchKernelGGL(sp::sidx_fill_kernel, dim3(nb), dim3(256), 0, stream, idx, tlen, cnt, off,

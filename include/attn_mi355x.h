@@ -144,7 +144,7 @@ attn_status attn_sparse_fwd(const void* q, const void* k, const void* v, const i
 
 /*
  * Workspace of attn_sparse_bwd: a per-row-block key histogram
- * (ceil(Nq/64) x Nkv int32), key offsets (Nkv + 1 int32), the transposed pair
+ * (ceil(Nq/16) x Nkv int32), key offsets (Nkv + 1 int32), the transposed pair
  * list (Nq x topk int32), dS (Nq x Hq/64 x ceil(topk/256)*256 x 64 bf16) and
  * each (row, head group, slot)'s dK/dV contribution (Nq x Hq/64 x topk x 1088
  * fp32; 9.1 GB at Hq = 64, Nq = 4096, topk = 512), each 256-byte aligned.

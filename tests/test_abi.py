@@ -130,10 +130,10 @@ def test_sparse_workspace_size(ea):
     # slots padded to 256) and the fp32 dK/dV contribution of every slot
     al = lambda x: (x + 255) // 256 * 256  # noqa: E731
     got = ea.attn_sparse_bwd_workspace_bytes(64, 4096, 4096, 512)
-    assert got == (al(64 * 4096 * 4) + al(4097 * 4) + al(4096 * 512 * 4) + al(4096 * 512 * 64 * 2)
+    assert got == (al(256 * 4096 * 4) + al(4097 * 4) + al(4096 * 512 * 4) + al(4096 * 512 * 64 * 2)
                    + al(4096 * 512 * 1088 * 4))
     assert ea.attn_sparse_bwd_workspace_bytes(128, 300, 280, 100) == (
-        al(5 * 280 * 4) + al(281 * 4) + al(300 * 100 * 4) + al(300 * 2 * 256 * 64 * 2)
+        al(19 * 280 * 4) + al(281 * 4) + al(300 * 100 * 4) + al(300 * 2 * 256 * 64 * 2)
         + al(300 * 2 * 100 * 1088 * 4))
     assert ea.attn_sparse_bwd_workspace_bytes(0, 0, 0, 8) == 0
 
