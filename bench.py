@@ -126,7 +126,7 @@ def _traffic():
 # HBM traffic from rocprofv3 counter passes
 # ----------------------------------------------------------------------------
 COPY_BYTES = 1 << 30             # the calibration copy moves 1 GiB each way
-MAIN_KERNEL = "bwd_dkdv_kernel"
+MAIN_KERNEL = "bwd_dkdv_w64_kernel"
 
 
 def copy_calibration():
@@ -447,7 +447,7 @@ def main(argv=None):
                     "tflops": round(tflops(fwd_flops(B, H, N, d, cfg.causal), fwd_ms), 3)},
         "roofline": {
             "bound": "mfma",
-            "kernel": "bwd_dkdv_kernel",
+            "kernel": MAIN_KERNEL,
             "achieved": round(main_tf, 3),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",

@@ -566,13 +566,21 @@ void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict_
     const int tc2 = (N + BC2 - 1) / BC2;
     const int tc = (N + BC - 1) / BC;            // 128-key tiles (dS^T and K image format)
     const int tr_count = (N + BR - 1) / BR;
-    // causal: key tile j has (N - 256 j) / 64 query tiles, so dispatch all
-    // heads' tile 0 first, then tile 1, ... (longest first); workgroups are
-    // dealt round-robin over the 8 XCDs, so when B*H is a multiple of 8 every
-    // tile of a head still runs on the same XCD.  Non-causal tiles are equal;
+    // causal: key tile j has (N - 256 j) / 64 query tiles.  Workgroups are
+    // dealt round-robin over the 8 XCDs (hardware index b runs on XCD b % 8);
+    // each XCD takes every eighth head and works through them two at a time,
+    // longest tiles first within each pair.  That balances the work like a
+    // global longest-first order while only about four heads' Q / dO are in
+    // use on an XCD at once (its L2 holds them).  Other head counts: all
+    // heads' tile 0 first, then tile 1, ...  Non-causal tiles are equal;
     // consecutive tiles of a head go to the same XCD.
     int bh, j;
-    if (CAUSAL) {
+    if (CAUSAL && BH % 16 == 0) {
+        const int x = blockIdx.x % 8, t = blockIdx.x / 8;
+        const int grp = t / (2 * tc2), r = t % (2 * tc2);
+        j = r / 2;
+        bh = (2 * grp + (r & 1)) * 8 + x;
+    } else if (CAUSAL) {
         bh = blockIdx.x % BH;
         j = blockIdx.x / BH;
     } else {
