@@ -21,9 +21,12 @@
 // order, so the results are bitwise reproducible.
 //
 // CDNA4 mapping (not the page's SM120 one):
-//  * dK/dV kernel: 512 threads = 8 wave64s (two per SIMD).  The workgroup owns
-//    B_c = 128 keys; wave (kw, qh) owns keys 32 kw .. + 31 and query rows
-//    32 qh .. + 31 of each 64-row query tile.
+//  * dK/dV kernel for d = 128 (bwd_dkdv_w64_kernel): 4 wave64s, one per SIMD,
+//    per 256-key tile; each wave owns 64 keys and every query row, keeps K in
+//    registers and dK / dV in the accumulation registers.
+//  * dK/dV kernel for other d (bwd_dkdv_kernel): 512 threads = 8 wave64s (two
+//    per SIMD).  The workgroup owns B_c = 128 keys; wave (kw, qh) owns keys
+//    32 kw .. + 31 and query rows 32 qh .. + 31 of each 64-row query tile.
 //  * S = Q K^T and dP = dO V^T take both operands from LDS.  Their accumulator
 //    layout (one key per lane) is exactly the A layout of P^T and dS^T, so
 //    dV = P^T dO and dK = dS^T Q take P and dS straight from registers, with

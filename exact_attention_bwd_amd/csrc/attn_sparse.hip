@@ -11,8 +11,9 @@
 // 64 (the M dimension of every product, as in the PR's design).
 //
 // CDNA4 mapping:
-//  * one workgroup per (query row, group of 64 heads); 4 wave64s, one per
-//    SIMD, with the whole 512-entry register file each.
+//  * one workgroup per (query row, group of 64 heads): 4 wave64s, one per
+//    SIMD, in the forward and the dQ kernel; 8 (two per SIMD) in the backward
+//    per-row kernel, so that one wave's MFMAs cover another's gather loads.
 //  * the gathered K rows feed the score products straight from memory (each
 //    lane's 16 bytes are one row-contiguous MFMA operand); V rows, Q_i, dO_i
 //    and K chunks that are read with a transposing LDS read are copied into
