@@ -37,7 +37,7 @@
 //    64-bank LDS.
 //  * P = exp(scale * S - L) is evaluated as 2^(S * scale * log2 e - L * log2 e)
 //    with v_exp_f32.
-//  * dQ kernel: 4 wave64s per (batch*head, 64-row query tile); dS^T tiles are
+//  * dQ kernel: 4 wave64s per (batch*head, 64-row query tile); dS tiles are
 //    copied into an LDS double buffer and read transposed, K comes from a
 //    register-ready image of K_j that the dK/dV kernel writes once per tile.
 #include <type_traits>
@@ -112,10 +112,7 @@ constexpr int NT = NW * 64;
 //    2..3 are r & 3, so the 4 rows x 4 chunks of one transposing read also land
 //    on 16 distinct chunks.  For HD = 64 (two rows per bank line) the same two
 //    properties hold per row parity.
-//  * dS^T [BC keys][BR queries] (workspace tiles, copied unchanged into the
-//    dQ kernel's LDS): the 8-byte unit u of row `key` lives at unit
-//    u ^ tswz(key), so 16 consecutive keys at the same unit, and 4 keys x 8
-//    units read by one transposing read, are on distinct banks.
+//  * dS tiles in the dQ kernel: see dst_lds_chunk.
 template <int HD>
 __device__ __forceinline__ int rswz(int r) {
     return HD == 128 ? (((r & 3) << 2) | ((r >> 2) & 3))
@@ -130,12 +127,6 @@ __device__ __forceinline__ int roff(int r, int c) {      // chunk c of row r (el
 template <int HD>
 __device__ __forceinline__ int roff4(int r, int col) {   // 4 elements at col (multiple of 4)
     return r * HD + ((((col >> 3) ^ rswz<HD>(r))) << 3) + (col & 4);
-}
-
-__device__ __forceinline__ int tswz(int key) { return ((key & 3) << 2) | ((key >> 2) & 3); }
-
-__device__ __forceinline__ int toff(int key, int u) {     // unit u (4 queries) of row key
-    return key * BR + ((u ^ tswz(key)) << 2);
 }
 
 template <int HD> struct Smem {
@@ -208,10 +199,27 @@ __device__ __forceinline__ void stage_bytes(const char* src, char* dst, int w, i
     }
 }
 
-// Workspace tile of dS^T for one (batch*head, query tile i, key tile j):
-// BC x BR bf16 in the swizzled dS^T layout (toff), so the dQ kernel can copy it
-// into LDS unchanged.
+// Workspace tile of dS for one (batch*head, query tile i, 128-key tile j),
+// BC x BR bf16 = 16 KiB, in the register order of its producer so that every
+// store is a whole 1 KiB run: block (qh, wh) = query rows 32 qh .. + 31 and
+// keys 64 wh .. + 63 is 4 KiB at (2 qh + wh) * 4 KiB; in it, 1 KiB run
+// c = 2 sk + k4 holds, for lane l = kl + 32 g, the 16 bytes of key
+// 64 wh + 32 sk + kl and query rows 32 qh + (2 k4 + e / 4) * 8 + 4 g + e % 4,
+// e = 0..7 (the C layout of an S / dP block, rows 16 k4 .. 16 k4 + 15,
+// rounded to bf16).
 constexpr int DST_EL = BC * BR;
+
+__device__ __forceinline__ int dst_run(int qh, int wh, int sk, int k4) {   // byte offset
+    return (2 * qh + wh) * 4096 + (2 * sk + k4) * 1024;
+}
+
+// The dQ kernel keeps a dS tile in LDS with its 16-byte chunks permuted by
+// dst_lds_chunk (an involution: bits 2..3 of the chunk index flip by bits
+// 6, 5), which makes its transposing reads (4 keys x 8 query units of 4
+// rows per half-wave) hit 32 distinct 8-byte bank slots.
+__device__ __forceinline__ int dst_lds_chunk(int c) {
+    return c ^ ((((c >> 6) & 1) << 3) | (((c >> 5) & 1) << 2));
+}
 
 __device__ __forceinline__ size_t dst_tile(int bh, int i, int j, int tr, int tc) {
     return ((size_t)((size_t)bh * tr + i) * tc + j) * DST_EL;
@@ -299,10 +307,6 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     // (offset ^ 16) and head-dim block db flips chunk bits 2..3 by db
     // (offset ^ (db << 5)).
     const int otr = roff4<HD>(qh * 32 + g * 4 + s4, hh * 16 + 4 * (t16 & 3));
-    // dS^T stores: this lane's key, units qh*8 + 2 rr + g of the workspace tile
-    int ow[4];
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) ow[rr] = toff(kw * 32 + l32, qh * 8 + rr * 2 + g);
     const int ol = qh * 32 + g * 4;              // L / D rows of this lane (+ 8 rr)
 
     const int it0 = CAUSAL ? (k0 / BR) : 0;
@@ -422,17 +426,16 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                 dk[db] = mfma32(k4 ? ds1 : ds0, bq, dk[db]);
             }
         }
-        // the next tile has landed and every read of this tile is done; the dS^T
+        // the next tile has landed and every read of this tile is done; the dS
         // stores go after the barrier so that its wait for the tile copies does
         // not also wait for them
         __syncthreads();
         const __amdgpu_buffer_rsrc_t dsr =
             make_rsrc(dSw + dst_tile(bh, it, j, tr_count, tc), DST_EL * 2);
-        const u32x4 d0 = __builtin_bit_cast(u32x4, ds0), d1 = __builtin_bit_cast(u32x4, ds1);
-        __builtin_amdgcn_raw_buffer_store_b64(u32x2{d0[0], d0[1]}, dsr, ow[0] * 2, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b64(u32x2{d0[2], d0[3]}, dsr, ow[1] * 2, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b64(u32x2{d1[0], d1[1]}, dsr, ow[2] * 2, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b64(u32x2{d1[2], d1[3]}, dsr, ow[3] * 2, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ds0), dsr,
+                                               dst_run(qh, kw >> 1, kw & 1, 0) + lane * 16, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ds1), dsr,
+                                               dst_run(qh, kw >> 1, kw & 1, 1) + lane * 16, 0, 0);
     }
 
     // ---- epilogue: the two waves sharing 32 keys (qh = 0, 1) add their partial
@@ -470,7 +473,7 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 // combining.  K_j stays in VGPRs as the B operand of S = Q K^T; V_j sits in
 // LDS; the dK / dV accumulators (64 keys x 128 columns each) take the
 // accumulation registers.  The two 32-row halves qb of a query tile are
-// processed one after the other.  dS^T tiles and the K image are written in
+// processed one after the other.  dS tiles and the K image are written in
 // the 128-key format the dQ kernel reads.
 // ----------------------------------------------------------------------------
 constexpr int BC2 = 256;                         // keys per workgroup
@@ -489,6 +492,16 @@ struct Smem2 {
     static_assert(BC2 * HD * 2 <= off_v, "K staging must fit below V");
 };
 
+// Compile-time loop: f(std::integral_constant<int, i>) for i = I .. N-1, so
+// that indices are constants (immediate offsets, if constexpr).
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
+
 // The S / dP products of this kernel are issued as VGPR-form MFMAs: with the
 // 256 dK / dV accumulator registers in the AGPR file, leaving the choice to the
 // compiler puts every MFMA result in AGPRs and overflows them.  Hazards this
@@ -503,8 +516,14 @@ __device__ __forceinline__ void mfma_v0(f32x16& c, const bf16x8& a, const bf16x8
     asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(c) : "v"(a), "v"(b));
 }
 
-__device__ __forceinline__ void mfma_v_settle(f32x16& a, f32x16& b, f32x16& c, f32x16& d) {
-    asm volatile("s_nop 15" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+__device__ __forceinline__ void mfma_v_settle2(f32x16& a, f32x16& b) {
+    asm volatile("s_nop 15" : "+v"(a), "+v"(b));
+}
+
+// dV / dK accumulation into the AGPR file; no VALU reads these registers
+// until acc_settle after the last one.
+__device__ __forceinline__ void mfma_a(f32x16& c, const bf16x8& a, const bf16x8& b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
 }
 
 // Transposing LDS reads issued from inline assembly.  The compiler treats its
@@ -529,6 +548,129 @@ __device__ __forceinline__ void tr_read4(u32x2& a, u32x2& b, u32x2& c, u32x2& d,
         : "=&v"(a), "=&v"(b), "=&v"(c), "=&v"(d)
         : "v"(pa), "v"(pb), "v"(pc), "v"(pd));
 }
+
+__device__ __forceinline__ void tr_read2(u32x2& a, u32x2& b, uint32_t pa, uint32_t pb) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %2\n\t"
+        "ds_read_b64_tr_b16 %1, %3"
+        : "=&v"(a), "=&v"(b)
+        : "v"(pa), "v"(pb));
+}
+
+template <int OFF>
+__device__ __forceinline__ void tr_read2o(u32x2& a, u32x2& b, uint32_t pa, uint32_t pb) {
+    static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %2 offset:%4\n\t"
+        "ds_read_b64_tr_b16 %1, %3 offset:%4"
+        : "=&v"(a), "=&v"(b)
+        : "v"(pa), "v"(pb), "n"(OFF));
+}
+
+template <int PENDING>
+__device__ __forceinline__ void tr_wait2(u32x2& a, u32x2& b) {
+    static_assert(PENDING >= 0 && PENDING <= 15, "pending count");
+    asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(PENDING));
+}
+
+// 16-byte LDS read at a + OFF, issued where it stands; lgkm_wait must follow
+// before the result is used.
+template <int OFF, typename T>
+__device__ __forceinline__ void lds_ld(T& d, uint32_t a) {
+    static_assert(sizeof(T) == 16 && OFF >= 0 && OFF < 65536, "b128 read");
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=&v"(d) : "v"(a), "n"(OFF));
+}
+
+// a ^ C, computed where it stands (C = 0: a itself)
+template <int C>
+__device__ __forceinline__ uint32_t vxor(uint32_t a) {
+    if constexpr (C == 0) {
+        return a;
+    } else {
+        uint32_t r;
+        asm volatile("v_xor_b32 %0, %1, %2" : "=v"(r) : "n"(C), "v"(a));
+        return r;
+    }
+}
+
+// s_waitcnt lgkmcnt(N) (N above 15 waits for 15, which is stricter), tied to
+// the registers whose loads it completes
+template <int N, typename A>
+__device__ __forceinline__ void lgkm_wait(A& a) {
+    static_assert(N >= 0, "wait count");
+    asm volatile("s_waitcnt lgkmcnt(%[n])" : "+v"(a) : [n] "n"(N > 15 ? 15 : N));
+}
+template <int N, typename A, typename B>
+__device__ __forceinline__ void lgkm_wait(A& a, B& b) {
+    static_assert(N >= 0, "wait count");
+    asm volatile("s_waitcnt lgkmcnt(%[n])" : "+v"(a), "+v"(b) : [n] "n"(N > 15 ? 15 : N));
+}
+template <int N, typename A, typename B, typename C>
+__device__ __forceinline__ void lgkm_wait(A& a, B& b, C& c) {
+    static_assert(N >= 0, "wait count");
+    asm volatile("s_waitcnt lgkmcnt(%[n])" : "+v"(a), "+v"(b), "+v"(c) : [n] "n"(N > 15 ? 15 : N));
+}
+
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
+// Issue order of the LDS reads of one 32-row half of the d = 128 dK/dV
+// kernel, so that every wait is exact.  A half starts with L row group 0 and
+// the 8 Q steps of S in flight (reads 0 .. 8); then per slot: S phase slot ks
+// reads the dP operands of step ks - 5 (dO, V block 0, V block 1); dP slot m
+// reads the transposed dO of dV steps 0 / 1 (m = 12 / 14), the dP operands of
+// step m / 2 + 3 (even m up to 8), L group m / 4 + 1 (m = 0, 4, 8) and D
+// groups 0 / 1 (m = 9 / 11); dV slot m reads D group m / 4 + 2 (m = 0, 4),
+// then (even m) the transposed reads of dV step m / 2 + 2 or dK step
+// m / 2 - 6; dK slot m (even, m < 12) the transposed Q of dK step m / 2 + 2.
+struct W64Sched {
+    static constexpr int KS = 8;
+    static constexpr int S_LD(int ks) { return ks >= KS - 3 ? 3 : 0; }
+    static constexpr int P_TR(int m) { return (m == 12 || m == 14) ? 2 : 0; }
+    static constexpr int P_DP(int m) { return (m % 2 == 0 && m / 2 + 3 < KS) ? 3 : 0; }
+    static constexpr int P_LV(int m) { return (m % 4 == 0 && m < 12) ? 1 : 0; }
+    static constexpr int P_DD(int m) { return (m == 9 || m == 11) ? 1 : 0; }
+    static constexpr int P_LD(int m) { return P_TR(m) + P_DP(m) + P_LV(m) + P_DD(m); }
+    static constexpr int V_DD(int m) { return (m == 0 || m == 4) ? 1 : 0; }
+    static constexpr int V_LD(int m) { return V_DD(m) + (m % 2 == 0 ? 2 : 0); }
+    static constexpr int K_LD(int m) { return (m % 2 == 0 && m / 2 + 2 < 8) ? 2 : 0; }
+    // reads issued up to and including slot ks / m of each phase
+    static constexpr int S_end(int ks) {
+        int n = 1 + KS;
+        for (int k = 0; k <= ks; ++k) n += S_LD(k);
+        return n;
+    }
+    static constexpr int P_end(int m) {
+        int n = S_end(KS - 1);
+        for (int i = 0; i <= m; ++i) n += P_LD(i);
+        return n;
+    }
+    static constexpr int V_end(int m) {
+        int n = P_end(15);
+        for (int i = 0; i <= m; ++i) n += V_LD(i);
+        return n;
+    }
+    static constexpr int K_end(int m) {
+        int n = V_end(15);
+        for (int i = 0; i <= m; ++i) n += K_LD(i);
+        return n;
+    }
+    // position of each read in the sequence (the later read of a pair)
+    static constexpr int i_aq(int ks) { return 1 + ks; }
+    static constexpr int i_lv(int rr) {
+        return rr == 0 ? 0 : P_end(4 * (rr - 1) - 1) + P_TR(4 * (rr - 1)) + P_DP(4 * (rr - 1));
+    }
+    static constexpr int i_ado(int ks) {
+        return ks < 3 ? S_end(ks + KS - 3 - 1) : P_end(2 * (ks - 3) - 1) + P_TR(2 * (ks - 3));
+    }
+    static constexpr int i_bv(int ks, int kb) { return i_ado(ks) + 1 + kb; }
+    static constexpr int i_dd(int rr) { return rr < 2 ? P_end(9 + 2 * rr - 1) : V_end(4 * (rr - 2) - 1); }
+    static constexpr int i_trv(int t) {
+        return (t == 0 ? P_end(11) : t == 1 ? P_end(13) : V_end(2 * (t - 2) - 1) + V_DD(2 * (t - 2))) + 1;
+    }
+    static constexpr int i_trk(int t) {
+        return (t < 2 ? V_end(2 * (t + 6) - 1) + V_DD(2 * (t + 6)) : K_end(2 * (t - 2) - 1)) + 1;
+    }
+};
 
 template <int PENDING>
 __device__ __forceinline__ void tr_wait(u32x2& a, u32x2& b, u32x2& c, u32x2& d) {
@@ -567,7 +709,7 @@ void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict_
     const int s4 = t16 >> 2;
 
     const int tc2 = (N + BC2 - 1) / BC2;
-    const int tc = (N + BC - 1) / BC;            // 128-key tiles (dS^T and K image format)
+    const int tc = (N + BC - 1) / BC;            // 128-key tiles (dS and K image format)
     const int tr_count = (N + BR - 1) / BR;
     // causal: key tile j has (N - 256 j) / 64 query tiles.  Workgroups are
     // dealt round-robin over the 8 XCDs (hardware index b runs on XCD b % 8);
@@ -673,11 +815,11 @@ void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict_
             dk[kb][b] = zero16();
         }
     const float sl2 = scale * kLog2e;
-    // dS^T stores: key row (w & 1) * 64 + 32 kb + l32 of 128-key tile 2 j + (w >> 1),
-    // units 8 qb + 2 rr + g (qb = 1 flips unit bit 3: offset ^ 32)
-    // unit 2 rr + g: offset ow0 ^ 8 rr
-    const int ow0 = toff((w & 1) * 64 + l32, g);
+    // dS stores: keys (w & 1) * 64 .. + 63 of 128-key tile 2 j + (w >> 1)
     const int jst = 2 * j + (w >> 1);
+    // row reads of V_j: this wave's rows, k step ks at ^ 32 ks bytes, key
+    // block 1 at + 8 KiB
+    const uint32_t aV = lds_addr(VS) + (uint32_t)((64 * w * HD + ob0) * 2);
 
     for (int it = it0, buf = 0; it < tr_count; ++it, buf ^= 1) {
         const int q0 = it * BR;
@@ -686,31 +828,84 @@ void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict_
         const __bf16* dOs = reinterpret_cast<const __bf16*>(smem + S::off_do) + buf * TILE_EL;
         const float* Ls = reinterpret_cast<const float*>(smem + S::off_l) + buf * BR;
         const float* Ds = reinterpret_cast<const float*>(smem + S::off_d) + buf * BR;
+        // dS stores go nowhere (buffer records 0) for a 128-key half past N
         const __amdgpu_buffer_rsrc_t dsr =
-            make_rsrc(dSw + dst_tile(bh, it, min(jst, tc - 1), tr_count, tc), DST_EL * 2);
+            make_rsrc(dSw + dst_tile(bh, it, min(jst, tc - 1), tr_count, tc), jst < tc ? DST_EL * 2 : 0);
+        // transposing-read bases of this tile: Q buffer + lane offset for the
+        // 4 column blocks x 2 row halves; dO, the row half qb and k4 are
+        // immediate offsets
+        uint32_t trv[DB][2];
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            trv[db][0] = lds_addr(Qs) + (uint32_t)((otr ^ (db << 5)) * 2);
+            trv[db][1] = lds_addr(Qs) + (uint32_t)((((otr + 8 * HD) ^ (db << 5)) ^ 16) * 2);
+        }
+        // row-read bases of this tile: Q rows of this lane (k step ks at
+        // ^ 32 ks bytes; dO at + 32 KiB, row half 1 at + 8 KiB) and L (D at
+        // + 512 bytes)
+        const uint32_t aQ = lds_addr(Qs) + (uint32_t)(ob0 * 2);
+        const uint32_t aL = lds_addr(Ls) + (uint32_t)(g * 16);
 
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            // ---- S = Q K^T, dP = dO V^T: 32 queries x 64 keys (two key blocks)
+        // L of row group 0 of half h and its Q operands for S, loaded ahead
+        f32x4 lv[4];
+        bf16x8 aq[KSD];
+        auto load_s = [&](auto hI) {
+            constexpr int h = decltype(hI)::value;
+            lds_ld<h * 128>(lv[0], aL);
+            static_for<0, KSD>([&](auto ksI) {
+                constexpr int ks = decltype(ksI)::value;
+                lds_ld<h * 8192>(aq[ks], vxor<ks * 32>(aQ));
+            });
+        };
+        load_s(std::integral_constant<int, 0>{});
+        static_for<0, 2>([&](auto qbI) {
+            constexpr int qb = decltype(qbI)::value;
+            using SC = W64Sched;
+            // A half runs four phases of 16 MFMAs: S, dP, dV, dK.  The
+            // softmax VALU work is spread over the dP phase (P and its bf16
+            // packing) and the dV phase (dS = P o (dP - D) and its packing),
+            // one share after each MFMA, so that it issues while the matrix
+            // core works on the previous product; each slot ends in a
+            // sched_barrier that keeps the compiler from regrouping it.
+            // Elements are taken in the order (row group rr, key block kb).
+            // Every LDS read is issued from assembly at a fixed point of
+            // this schedule and waited for with the count W64Sched derives.
+            f32x4 dd[4];
+            bf16x8 ado[KSD], bv[KSD][2];
+            auto load_dp = [&](auto ksI) {
+                constexpr int ks = decltype(ksI)::value;
+                lds_ld<2 * S::TILE + qb * 8192>(ado[ks], vxor<ks * 32>(aQ));
+                const uint32_t av = vxor<ks * 32>(aV);
+                lds_ld<0>(bv[ks][0], av);
+                lds_ld<8192>(bv[ks][1], av);
+            };
+            auto load_dd = [&](auto rrI) {
+                constexpr int rr = decltype(rrI)::value;
+                lds_ld<512 + qb * 128 + rr * 32>(dd[rr], aL);
+            };
+            // step t = 4 k4 + db of the dV (src dO) or dK (src Q) phase
+            u32x2 tb[8][2];
+            auto tr_step = [&](auto tI, auto doI) {
+                constexpr int t = decltype(tI)::value, db = t & 3, k4 = t >> 2;
+                constexpr int off = (qb * 32 * HD + k4 * 16 * HD) * 2 + (decltype(doI)::value ? 2 * S::TILE : 0);
+                tr_read2o<off>(tb[t][0], tb[t][1], trv[db][0], trv[db][1]);
+            };
+            using IsDo = std::integral_constant<int, 1>;
+            using IsQ = std::integral_constant<int, 0>;
             f32x16 s[2], dp[2];
-#pragma unroll
-            for (int ks = 0; ks < KSD; ++ks) {
-                const int oa = (ob0 ^ (ks * 16)) + qb * 32 * HD;
-                const bf16x8 aq = lds_read16(Qs + oa);
-                const bf16x8 ado = lds_read16(dOs + oa);
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const bf16x8 bv = lds_read16(VS + (ob0 ^ (ks * 16)) + (64 * w + 32 * kb) * HD);
-                    if (ks == 0) {
-                        mfma_v0(s[kb], aq, kreg[kb][ks]);
-                        mfma_v0(dp[kb], ado, bv);
-                    } else {
-                        mfma_v(s[kb], aq, kreg[kb][ks]);
-                        mfma_v(dp[kb], ado, bv);
-                    }
-                }
-            }
-            mfma_v_settle(s[0], s[1], dp[0], dp[1]);
+            // ---- S = Q K^T: 32 queries x 64 keys
+            static_for<0, KSD>([&](auto ksI) {
+                constexpr int ks = decltype(ksI)::value;
+                lgkm_wait<SC::S_end(ks - 1) - 1 - SC::i_aq(ks)>(aq[ks]);
+                static_for<0, 2>([&](auto kbI) {
+                    constexpr int kb = decltype(kbI)::value;
+                    if constexpr (ks == 0) mfma_v0(s[kb], aq[ks], kreg[kb][ks]);
+                    else mfma_v(s[kb], aq[ks], kreg[kb][ks]);
+                });
+                if constexpr (SC::S_LD(ks) > 0) load_dp(std::integral_constant<int, ks - (KSD - 3)>{});
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            mfma_v_settle2(s[0], s[1]);
             __builtin_amdgcn_sched_barrier(0);
             // ---- masking where this block's keys reach past its first query
             //      row (causal diagonal) or past the end
@@ -728,82 +923,80 @@ void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict_
                     }
                 }
             }
-            // ---- P = exp(scale S - L), dS = P o (dP - D)
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const f32x4 lv = *reinterpret_cast<const f32x4*>(Ls + 32 * qb + g * 4 + rr * 8);
-                const f32x4 dd = *reinterpret_cast<const f32x4*>(Ds + 32 * qb + g * 4 + rr * 8);
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = rr * 4 + e;
-                        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], sl2, -lv[e]));
-                        s[kb][r] = p;
-                        dp[kb][r] = p * (dp[kb][r] - dd[e]);
-                    }
-            }
+            __builtin_amdgcn_sched_barrier(0);
+            // ---- dP = dO V^T; VALU slots: P = 2^(S scale log2 e - L log2 e)
             bf16x8 pa[2][2], da[2][2];
+            static_for<0, 16>([&](auto mI) {
+                constexpr int m = decltype(mI)::value, ks = m >> 1, kb = m & 1, rr = m >> 2;
+                if constexpr (m == 12) tr_step(std::integral_constant<int, 0>{}, IsDo{});
+                if constexpr (m == 14) tr_step(std::integral_constant<int, 1>{}, IsDo{});
+                if constexpr (SC::P_DP(m) > 0) load_dp(std::integral_constant<int, ks + 3>{});
+                if constexpr (SC::P_LV(m) > 0) lds_ld<qb * 128 + (rr + 1) * 32>(lv[rr + 1], aL);
+                if constexpr (SC::P_DD(m) > 0) load_dd(std::integral_constant<int, ((m - 9) >> 1)>{});
+                lgkm_wait<SC::P_end(m) - 1 - cmax(SC::i_bv(ks, kb), SC::i_lv(rr))>(ado[ks], bv[ks][kb], lv[rr]);
+                if constexpr (ks == 0) mfma_v0(dp[kb], ado[ks], bv[ks][kb]);
+                else mfma_v(dp[kb], ado[ks], bv[ks][kb]);
+                constexpr int ekb = (m >> 1) & 1;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                pa[kb][0] = pack_c8(s[kb], 0);
-                pa[kb][1] = pack_c8(s[kb], 8);
-                da[kb][0] = pack_c8(dp[kb], 0);
-                da[kb][1] = pack_c8(dp[kb], 8);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            // ---- dS^T for the dQ kernel
-            if (jst < tc) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const u32x4 d0 = __builtin_bit_cast(u32x4, da[kb][0]);
-                    const u32x4 d1 = __builtin_bit_cast(u32x4, da[kb][1]);
-                    const int kro = kb * 32 * BR;
-                    __builtin_amdgcn_raw_buffer_store_b64(u32x2{d0[0], d0[1]}, dsr, (((ow0 ^ (0 * 8)) + kro) ^ (qb * 32)) * 2, 0, 0);
-                    __builtin_amdgcn_raw_buffer_store_b64(u32x2{d0[2], d0[3]}, dsr, (((ow0 ^ (1 * 8)) + kro) ^ (qb * 32)) * 2, 0, 0);
-                    __builtin_amdgcn_raw_buffer_store_b64(u32x2{d1[0], d1[1]}, dsr, (((ow0 ^ (2 * 8)) + kro) ^ (qb * 32)) * 2, 0, 0);
-                    __builtin_amdgcn_raw_buffer_store_b64(u32x2{d1[2], d1[3]}, dsr, (((ow0 ^ (3 * 8)) + kro) ^ (qb * 32)) * 2, 0, 0);
+                for (int x = 0; x < 2; ++x) {
+                    const int r = 4 * rr + 2 * (m & 1) + x;
+                    s[ekb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[ekb][r], sl2, -lv[rr][r & 3]));
                 }
-            }
+                if constexpr (m == 8 || m == 9) pa[m - 8][0] = pack_c8(s[m - 8], 0);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            mfma_v_settle2(dp[0], dp[1]);
             __builtin_amdgcn_sched_barrier(0);
-            // ---- dV += P^T dO, dK += dS^T Q over these 32 queries; the B
-            //      operand of each (db, k4) feeds both key blocks
-            {
-                const uint32_t aq = lds_addr(Qs), ado = lds_addr(dOs);
-                auto addr = [&](int step, uint32_t base, int half) -> uint32_t {
-                    const int db = step >> 1, k4 = step & 1;
-                    const int o = half ? (((otr + 8 * HD) ^ (db << 5) ^ 16)) : (otr ^ (db << 5));
-                    return base + (uint32_t)((o + qb * 32 * HD + k4 * 16 * HD) * 2);
-                };
-                u32x2 c0, c1, c2, c3, n0, n1, n2, n3;
-                tr_read4(c0, c1, c2, c3, addr(0, ado, 0), addr(0, ado, 1), addr(0, aq, 0), addr(0, aq, 1));
-#pragma unroll
-                for (int step = 0; step < 2 * DB; ++step) {
-                    const int db = step >> 1, k4 = step & 1;
-                    if (step + 1 < 2 * DB) {
-                        tr_read4(n0, n1, n2, n3, addr(step + 1, ado, 0), addr(step + 1, ado, 1),
-                                 addr(step + 1, aq, 0), addr(step + 1, aq, 1));
-                        tr_wait<4>(c0, c1, c2, c3);
-                    } else {
-                        tr_wait<0>(c0, c1, c2, c3);
-                    }
-                    const bf16x8 bo = cat_u(c0, c1), bq = cat_u(c2, c3);
-#pragma unroll
-                    for (int kb = 0; kb < 2; ++kb) {
-                        dv[kb][db] = mfma32(pa[kb][k4], bo, dv[kb][db]);
-                        dk[kb][db] = mfma32(da[kb][k4], bq, dk[kb][db]);
-                    }
-                    c0 = n0;
-                    c1 = n1;
-                    c2 = n2;
-                    c3 = n3;
+            // ---- dV += P^T dO; VALU slots: dS = P o (dP - D)
+            static_for<0, 16>([&](auto mI) {
+                constexpr int m = decltype(mI)::value, t = m >> 1, kb = m & 1, rr = m >> 2;
+                if constexpr (SC::V_DD(m) > 0) load_dd(std::integral_constant<int, rr + 2>{});
+                if constexpr (kb == 0) {
+                    // two steps of reads stay in flight: this phase's, then
+                    // the first two of the dK phase
+                    if constexpr (t + 2 < 8) tr_step(std::integral_constant<int, t + 2>{}, IsDo{});
+                    else tr_step(std::integral_constant<int, t - 6>{}, IsQ{});
                 }
-            }
-        }
+                lgkm_wait<SC::V_end(m) - 1 - cmax(SC::i_trv(t), SC::i_dd(rr))>(tb[t][0], tb[t][1], dd[rr]);
+                if constexpr (m == 0 || m == 1) pa[m][1] = pack_c8(s[m], 8);
+                mfma_a(dv[kb][t & 3], pa[kb][t >> 2], cat_u(tb[t][0], tb[t][1]));
+                constexpr int ekb = (m >> 1) & 1;
+#pragma unroll
+                for (int x = 0; x < 2; ++x) {
+                    const int r = 4 * rr + 2 * (m & 1) + x;
+                    dp[ekb][r] = s[ekb][r] * (dp[ekb][r] - dd[rr][r & 3]);
+                }
+                if constexpr (m == 8 || m == 9) da[m - 8][0] = pack_c8(dp[m - 8], 0);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            // ---- dK += dS^T Q; dS stores for the dQ kernel
+            static_for<0, 16>([&](auto mI) {
+                constexpr int m = decltype(mI)::value, t = m >> 1, kb = m & 1;
+                if constexpr (SC::K_LD(m) > 0) tr_step(std::integral_constant<int, t + 2>{}, IsQ{});
+                lgkm_wait<SC::K_end(m) - 1 - SC::i_trk(t)>(tb[t][0], tb[t][1]);
+                if constexpr (m == 0 || m == 1) da[m][1] = pack_c8(dp[m], 8);
+                if constexpr (m >= 2 && m < 6) {
+                    // run (sk, k4) = (0, 0) (1, 0) (0, 1) (1, 1) of this wave's block
+                    constexpr int sk = m & 1, k4 = (m - 2) >> 1;
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, da[sk][k4]), dsr,
+                                                           dst_run(qb, w & 1, sk, k4) + lane * 16, 0, 0);
+                }
+                mfma_a(dk[kb][t & 3], da[kb][t >> 2], cat_u(tb[t][0], tb[t][1]));
+                // the next half's L and Q operands, after the last wait
+                if constexpr (qb == 0 && m == 15) load_s(std::integral_constant<int, 1>{});
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        });
         __syncthreads();                         // next tile landed; this one free
     }
 
-    // ---- epilogue: dV, dK (scaled) of this wave's 64 keys
+    // ---- epilogue: dV, dK (scaled) of this wave's 64 keys, once the last
+    //      accumulations have left the matrix core
+    asm volatile("s_nop 15\n\ts_nop 15"
+                 : "+a"(dv[0][0]), "+a"(dv[0][1]), "+a"(dv[0][2]), "+a"(dv[0][3]),
+                   "+a"(dv[1][0]), "+a"(dv[1][1]), "+a"(dv[1][2]), "+a"(dv[1][3]),
+                   "+a"(dk[0][0]), "+a"(dk[0][1]), "+a"(dk[0][2]), "+a"(dk[0][3]),
+                   "+a"(dk[1][0]), "+a"(dk[1][1]), "+a"(dk[1][2]), "+a"(dk[1][3]));
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -821,7 +1014,7 @@ void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict_
 
 // ----------------------------------------------------------------------------
 // Kernel B: dQ_i = scale * sum_j dS_ij K_j, one workgroup of 4 wave64s per
-// (batch*head, 64-row query tile i).  The dS^T tiles written by kernel A are
+// (batch*head, 64-row query tile i).  The dS tiles written by kernel A are
 // copied into an LDS double buffer one step ahead and read transposed (A
 // operands); the B operands come straight from the K image in registers, one
 // step ahead.  With 32 KiB of LDS per workgroup several workgroups share a CU,
@@ -836,7 +1029,7 @@ void bwd_dq_kernel(const __bf16* __restrict__ Kimg, const __bf16* __restrict__ d
                    __bf16* __restrict__ dQ, int BH, int N, float scale) {
     constexpr int DB = HD / 32;
     constexpr int TQ = 2 * DB / QW;              // 32 x 32 dQ blocks per wave (2 or 1)
-    constexpr int DS_B = DST_EL * 2;             // one dS^T tile (bytes)
+    constexpr int DS_B = DST_EL * 2;             // one dS tile (bytes)
     __shared__ __attribute__((aligned(16))) char smem[2 * DS_B];
 
     const int lane = threadIdx.x & 63;
@@ -857,22 +1050,26 @@ void bwd_dq_kernel(const __bf16* __restrict__ Kimg, const __bf16* __restrict__ d
     const int q0 = i * BR;
     const int j_end = CAUSAL ? min(tc, (min(q0 + BR, N) - 1) / BC + 1) : tc;
 
-    // transposing-read offsets into a dS^T tile: keys 16 ks + 8 g + s4 (+4),
-    // queries of query block qb (plus a constant per ks)
+    // transposing reads of the A operand (dS, query rows x keys): the lanes
+    // of a 16-lane group address keys 16 ks + 8 g + s4 (+ 4) and the 8-byte
+    // half (t16 >> 1) & 1 of query unit 4 hh + (t16 & 3) of query block qb;
+    // the step ks adds a constant (keys 16 ks: chunk + 16 (ks & 1) +
+    // 128 ((ks >> 1) & 1) + 256 (ks >> 2))
     int ods[TQ][2];
 #pragma unroll
-    for (int t = 0; t < TQ; ++t) {
-        const int u = (qb0 + t) * 8 + hh * 4 + (t16 & 3);
-        ods[t][0] = toff(g * 8 + s4, u);
-        ods[t][1] = toff(g * 8 + 4 + s4, u);
-    }
+    for (int t = 0; t < TQ; ++t)
+#pragma unroll
+        for (int h4 = 0; h4 < 2; ++h4) {
+            const int c = (qb0 + t) * 512 + hh * 64 + 32 * (t16 & 1) + g * 8 + h4 * 4 + s4;
+            ods[t][h4] = (dst_lds_chunk(c) * 16 + ((t16 >> 1) & 1) * 8) / 2;   // elements
+        }
 
     auto stage = [&](int jj, int buf) {
         const __amdgpu_buffer_rsrc_t r = make_rsrc(dSw + dst_tile(bh, i, jj, tr_count, tc), DS_B);
 #pragma unroll
         for (int k = 0; k < DS_B / 1024 / QW; ++k) {
             const int I = w * (DS_B / 1024 / QW) + k;
-            bdma16(r, I * 1024 + lane * 16, smem + buf * DS_B + I * 1024);
+            bdma16(r, dst_lds_chunk(I * 64 + lane) * 16, smem + buf * DS_B + I * 1024);
         }
     };
     auto load_k = [&](int jj, bf16x8* kb) {
@@ -902,8 +1099,8 @@ void bwd_dq_kernel(const __bf16* __restrict__ Kimg, const __bf16* __restrict__ d
         for (int ks = 0; ks < BC / 16; ++ks) {
 #pragma unroll
             for (int t = 0; t < TQ; ++t) {
-                const bf16x8 a = cat44(lds_read_tr(dST + ods[t][0] + ks * 16 * BR),
-                                       lds_read_tr(dST + ods[t][1] + ks * 16 * BR));
+                const int kso = (256 * (ks & 1) + 2048 * ((ks >> 1) & 1) + 4096 * (ks >> 2)) / 2;
+                const bf16x8 a = cat44(lds_read_tr(dST + ods[t][0] + kso), lds_read_tr(dST + ods[t][1] + kso));
                 acc[t] = mfma32(a, kcur[ks], acc[t]);
             }
         }
@@ -956,8 +1153,8 @@ hipError_t launch_bwd_preprocess(const void* o, const void* dO, float* D, int BH
     return hipGetLastError();
 }
 
-// Workspace: [Lb BH x n_pad fp32][D BH x n_pad fp32][dS^T tiles BH x T_r x T_c
-// x (BC x BR) bf16][K image BH x T_c x (BC x d) bf16].  Every dS^T tile the dQ
+// Workspace: [Lb BH x n_pad fp32][D BH x n_pad fp32][dS tiles BH x T_r x T_c
+// x (BC x BR) bf16][K image BH x T_c x (BC x d) bf16].  Every dS tile the dQ
 // kernel reads is written by the dK/dV kernel first (causal: exactly the tiles
 // with j <= i / 2), and so is every K image tile.
 static size_t n_pad_of(int N) { return (size_t)((N + bwd::BR - 1) / bwd::BR) * bwd::BR; }
