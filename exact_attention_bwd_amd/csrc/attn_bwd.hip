@@ -613,6 +613,24 @@ __device__ __forceinline__ void lgkm_wait(A& a, B& b, C& c) {
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
+// 16-byte global load at base + voff + OFF (OFF < 4096), issued where it
+// stands; vm_wait must follow before the result is used.
+template <int OFF>
+__device__ __forceinline__ void gload16(bf16x8& d, const void* base, uint32_t voff) {
+    static_assert(OFF >= 0 && OFF < 4096, "global offset field");
+    asm volatile("global_load_dwordx4 %0, %1, %2 offset:%3" : "=&v"(d) : "v"(voff), "s"(base), "n"(OFF));
+}
+
+// s_waitcnt vmcnt(N), tied to the eight registers whose loads it completes
+template <int N>
+__device__ __forceinline__ void vm_wait(bf16x8* r) {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    asm volatile("s_waitcnt vmcnt(%[n])"
+                 : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]), "+v"(r[6]), "+v"(r[7])
+                 : [n] "n"(N)
+                 : "memory");
+}
+
 // Issue order of the LDS reads of one 32-row half of the d = 128 dK/dV
 // kernel, so that every wait is exact.  A half starts with L row group 0 and
 // the 8 Q steps of S in flight (reads 0 .. 8); then per slot: S phase slot ks
@@ -803,7 +821,10 @@ void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict_
         if (w == 0) bdma4(make_rsrc(Lbh + q0, BR * 4), lane * 4, smem + S::off_l + buf * BR * 4);
         if (w == 1) bdma4(make_rsrc(Dph + q0, BR * 4), lane * 4, smem + S::off_d + buf * BR * 4);
     };
-    stage_tile(it0, 0);
+    // query tiles are walked from the last one down to the diagonal: the
+    // workgroups of one head then read the same Q_i / dO_i at the same time,
+    // and the shared L2 serves all but the first
+    stage_tile(tr_count - 1, 0);
     __syncthreads();
 
     f32x16 dv[2][DB], dk[2][DB];
@@ -821,9 +842,9 @@ void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict_
     // block 1 at + 8 KiB
     const uint32_t aV = lds_addr(VS) + (uint32_t)((64 * w * HD + ob0) * 2);
 
-    for (int it = it0, buf = 0; it < tr_count; ++it, buf ^= 1) {
+    for (int it = tr_count - 1, buf = 0; it >= it0; --it, buf ^= 1) {
         const int q0 = it * BR;
-        if (it + 1 < tr_count) stage_tile(it + 1, buf ^ 1);     // lands during this iteration
+        if (it - 1 >= it0) stage_tile(it - 1, buf ^ 1);     // lands during this iteration
         const __bf16* Qs = reinterpret_cast<const __bf16*>(smem + S::off_q) + buf * TILE_EL;
         const __bf16* dOs = reinterpret_cast<const __bf16*>(smem + S::off_do) + buf * TILE_EL;
         const float* Ls = reinterpret_cast<const float*>(smem + S::off_l) + buf * BR;
@@ -933,7 +954,13 @@ void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict_
                 if constexpr (SC::P_DP(m) > 0) load_dp(std::integral_constant<int, ks + 3>{});
                 if constexpr (SC::P_LV(m) > 0) lds_ld<qb * 128 + (rr + 1) * 32>(lv[rr + 1], aL);
                 if constexpr (SC::P_DD(m) > 0) load_dd(std::integral_constant<int, ((m - 9) >> 1)>{});
-                lgkm_wait<SC::P_end(m) - 1 - cmax(SC::i_bv(ks, kb), SC::i_lv(rr))>(ado[ks], bv[ks][kb], lv[rr]);
+                // each register is tied to the first wait that covers it only
+                if constexpr (kb == 1)
+                    lgkm_wait<SC::P_end(m) - 1 - SC::i_bv(ks, 1)>(bv[ks][1]);
+                else if constexpr ((m & 3) == 0)
+                    lgkm_wait<SC::P_end(m) - 1 - cmax(SC::i_bv(ks, 0), SC::i_lv(rr))>(ado[ks], bv[ks][0], lv[rr]);
+                else
+                    lgkm_wait<SC::P_end(m) - 1 - SC::i_bv(ks, 0)>(ado[ks], bv[ks][0]);
                 if constexpr (ks == 0) mfma_v0(dp[kb], ado[ks], bv[ks][kb]);
                 else mfma_v(dp[kb], ado[ks], bv[ks][kb]);
                 constexpr int ekb = (m >> 1) & 1;
@@ -957,7 +984,10 @@ void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict_
                     if constexpr (t + 2 < 8) tr_step(std::integral_constant<int, t + 2>{}, IsDo{});
                     else tr_step(std::integral_constant<int, t - 6>{}, IsQ{});
                 }
-                lgkm_wait<SC::V_end(m) - 1 - cmax(SC::i_trv(t), SC::i_dd(rr))>(tb[t][0], tb[t][1], dd[rr]);
+                if constexpr ((m & 3) == 0)
+                    lgkm_wait<SC::V_end(m) - 1 - cmax(SC::i_trv(t), SC::i_dd(rr))>(tb[t][0], tb[t][1], dd[rr]);
+                else if constexpr (kb == 0)
+                    lgkm_wait<SC::V_end(m) - 1 - SC::i_trv(t)>(tb[t][0], tb[t][1]);
                 if constexpr (m == 0 || m == 1) pa[m][1] = pack_c8(s[m], 8);
                 mfma_a(dv[kb][t & 3], pa[kb][t >> 2], cat_u(tb[t][0], tb[t][1]));
                 constexpr int ekb = (m >> 1) & 1;
@@ -973,7 +1003,7 @@ void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict_
             static_for<0, 16>([&](auto mI) {
                 constexpr int m = decltype(mI)::value, t = m >> 1, kb = m & 1;
                 if constexpr (SC::K_LD(m) > 0) tr_step(std::integral_constant<int, t + 2>{}, IsQ{});
-                lgkm_wait<SC::K_end(m) - 1 - SC::i_trk(t)>(tb[t][0], tb[t][1]);
+                if constexpr (kb == 0) lgkm_wait<SC::K_end(m) - 1 - SC::i_trk(t)>(tb[t][0], tb[t][1]);
                 if constexpr (m == 0 || m == 1) da[m][1] = pack_c8(dp[m], 8);
                 if constexpr (m >= 2 && m < 6) {
                     // run (sk, k4) = (0, 0) (1, 0) (0, 1) (1, 1) of this wave's block
@@ -1014,12 +1044,15 @@ void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict_
 
 // ----------------------------------------------------------------------------
 // Kernel B: dQ_i = scale * sum_j dS_ij K_j, one workgroup of 4 wave64s per
-// (batch*head, 64-row query tile i).  The dS tiles written by kernel A are
-// copied into an LDS double buffer one step ahead and read transposed (A
-// operands); the B operands come straight from the K image in registers, one
-// step ahead.  With 32 KiB of LDS per workgroup several workgroups share a CU,
-// which hides the memory latency.  The reduction over key tiles happens in
-// fp32 registers (no atomics).
+// (batch*head, pair of 64-row query tiles i0 = 2 p, i1 = 2 p + 1), so that
+// every K image tile loaded serves 128 query rows (both tiles of a pair see
+// the same key tiles, also when causal).  Wave w owns head-dim columns
+// 32 (w % DB) .. + 31 and TQ = 4 DB / 4 blocks of 32 rows.  Per key step the
+// two dS tiles are copied into one of two LDS stages (the next step's copy
+// runs during this step's products) and read transposed (A operands); the
+// wave's K image slice comes into registers, also one step ahead.  Two
+// workgroups share a CU.  The reduction over key tiles happens in fp32
+// registers (no atomics).
 // ----------------------------------------------------------------------------
 constexpr int QW = 4;                            // waves per dQ workgroup
 
@@ -1028,14 +1061,17 @@ __global__ __attribute__((amdgpu_flat_work_group_size(QW * 64, QW * 64)))
 void bwd_dq_kernel(const __bf16* __restrict__ Kimg, const __bf16* __restrict__ dSw,
                    __bf16* __restrict__ dQ, int BH, int N, float scale) {
     constexpr int DB = HD / 32;
-    constexpr int TQ = 2 * DB / QW;              // 32 x 32 dQ blocks per wave (2 or 1)
+    constexpr int TQ = 4 * DB / QW;              // 32-row query blocks per wave (4 or 2)
     constexpr int DS_B = DST_EL * 2;             // one dS tile (bytes)
-    __shared__ __attribute__((aligned(16))) char smem[2 * DS_B];
+    constexpr int STB = 2 * DS_B;                // one stage: the pair's two tiles
+    constexpr int NST = 2;
+    constexpr int KS = BC / 16;                  // k steps per key tile
+    __shared__ __attribute__((aligned(16))) char smem[NST * STB];
 
     const int lane = threadIdx.x & 63;
     const int w = wave_id();
     const int db = w % DB;                       // this wave's 32 head-dim columns
-    const int qb0 = (TQ == 2) ? 0 : (w / DB);    // its first 32-row query block
+    const int qb0 = (w / DB) * TQ;               // its first 32-row block of the pair
     const int g = lane >> 5;
     const int t16 = lane & 15;
     const int hh = (lane >> 4) & 1;
@@ -1043,73 +1079,106 @@ void bwd_dq_kernel(const __bf16* __restrict__ Kimg, const __bf16* __restrict__ d
 
     const int tc = (N + BC - 1) / BC;
     const int tr_count = (N + BR - 1) / BR;
-    const int logical = xcd_remap(blockIdx.x, BH * tr_count);
-    const int bh = logical / tr_count;
-    // causal: the last query tiles see the most key tiles, so they go first
-    const int i = CAUSAL ? (tr_count - 1 - logical % tr_count) : (logical % tr_count);
-    const int q0 = i * BR;
-    const int j_end = CAUSAL ? min(tc, (min(q0 + BR, N) - 1) / BC + 1) : tc;
+    const int tp = (tr_count + 1) / 2;
+    const int logical = xcd_remap(blockIdx.x, BH * tp);
+    const int bh = logical / tp;
+    // causal: the last pairs see the most key tiles, so they go first
+    const int pr = CAUSAL ? (tp - 1 - logical % tp) : (logical % tp);
+    const int i0 = 2 * pr;
+    const bool has_i1 = i0 + 1 < tr_count;
+    const int q0 = i0 * BR;
+    const int j_end = CAUSAL ? min(tc, (min(q0 + 2 * BR, N) - 1) / BC + 1) : tc;
 
-    // transposing reads of the A operand (dS, query rows x keys): the lanes
-    // of a 16-lane group address keys 16 ks + 8 g + s4 (+ 4) and the 8-byte
-    // half (t16 >> 1) & 1 of query unit 4 hh + (t16 & 3) of query block qb;
-    // the step ks adds a constant (keys 16 ks: chunk + 16 (ks & 1) +
-    // 128 ((ks >> 1) & 1) + 256 (ks >> 2))
-    int ods[TQ][2];
+    // transposing reads of the A operand (dS, query rows x keys): for block
+    // qb = qb0 + t (tile qb / 2, its block qb % 2) the lanes of a 16-lane
+    // group address keys 16 ks + 8 g + s4 (+ 4) and the 8-byte half
+    // (t16 >> 1) & 1 of query unit 4 hh + (t16 & 3); the stage and the k step
+    // (keys 16 ks: chunk + 16 (ks & 1) + 128 ((ks >> 1) & 1) + 256 (ks >> 2))
+    // are immediate offsets
+    uint32_t tra[TQ][2];
 #pragma unroll
     for (int t = 0; t < TQ; ++t)
 #pragma unroll
         for (int h4 = 0; h4 < 2; ++h4) {
-            const int c = (qb0 + t) * 512 + hh * 64 + 32 * (t16 & 1) + g * 8 + h4 * 4 + s4;
-            ods[t][h4] = (dst_lds_chunk(c) * 16 + ((t16 >> 1) & 1) * 8) / 2;   // elements
+            const int qb = qb0 + t;
+            const int c = (qb & 1) * 512 + hh * 64 + 32 * (t16 & 1) + g * 8 + h4 * 4 + s4;
+            tra[t][h4] = lds_addr(smem) + (uint32_t)((qb >> 1) * DS_B + dst_lds_chunk(c) * 16 + ((t16 >> 1) & 1) * 8);
         }
 
-    auto stage = [&](int jj, int buf) {
-        const __amdgpu_buffer_rsrc_t r = make_rsrc(dSw + dst_tile(bh, i, jj, tr_count, tc), DS_B);
+    // the pair's two dS tiles of key tile jj into stage st (the second reads
+    // as zero when the pair has one tile)
+    auto stage = [&](int jj, int st) {
 #pragma unroll
-        for (int k = 0; k < DS_B / 1024 / QW; ++k) {
-            const int I = w * (DS_B / 1024 / QW) + k;
-            bdma16(r, dst_lds_chunk(I * 64 + lane) * 16, smem + buf * DS_B + I * 1024);
+        for (int k = 0; k < STB / 1024 / QW; ++k) {
+            const int I = w * (STB / 1024 / QW) + k;           // 1 KiB block of the stage
+            const int t2 = I / (DS_B / 1024);
+            const int Ib = I % (DS_B / 1024);
+            const bool ok = t2 == 0 || has_i1;
+            const __amdgpu_buffer_rsrc_t r =
+                make_rsrc(dSw + dst_tile(bh, ok ? i0 + t2 : i0, jj, tr_count, tc), ok ? DS_B : 0);
+            bdma16(r, dst_lds_chunk(Ib * 64 + lane) * 16, smem + st * STB + I * 1024);
         }
     };
+    // K image loads from assembly: the compiler cannot follow which register
+    // set a load in flight belongs to and would wait for the newest ones; the
+    // step's own vmcnt wait covers them
+    const uint32_t kvo = (uint32_t)((db * KS * 64 + lane) * 16);
     auto load_k = [&](int jj, bf16x8* kb) {
-        const __amdgpu_buffer_rsrc_t r = make_rsrc(Kimg + kimg_tile(bh, jj, tc, HD), BC * HD * 2);
-#pragma unroll
-        for (int ks = 0; ks < BC / 16; ++ks)
-            kb[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                                                    r, ((db * (BC / 16) + ks) * 64 + lane) * 16, 0, 0));
+        const __bf16* kt = Kimg + kimg_tile(bh, jj, tc, HD);
+        static_for<0, KS>([&](auto ksI) {
+            constexpr int ks = decltype(ksI)::value;
+            gload16<(ks & 3) * 1024>(kb[ks], kt, kvo + (ks >> 2) * 4096);
+        });
     };
 
-    bf16x8 kcur[BC / 16], knext[BC / 16];
-    stage(0, 0);
-    load_k(0, kcur);
-    __syncthreads();
-
+    // Steps run one ahead: step jj's tiles sit in LDS stage jj % 2 and its K
+    // slice in kb[jj % 2].  Every step, including a padding step that rounds
+    // the loop up to an even count (it computes nothing), issues the loads of
+    // step jj + 1 (the last real step when past the end), so at the start of
+    // step jj exactly its own loads are in flight.  No load is conditional: a
+    // register set written on one path only would make the compiler copy it
+    // while its load may still be in flight.
+    bf16x8 kb[NST][KS];
     f32x16 acc[TQ];
 #pragma unroll
     for (int t = 0; t < TQ; ++t) acc[t] = zero16();
-    for (int jj = 0, buf = 0; jj < j_end; ++jj, buf ^= 1) {
-        const bool more = jj + 1 < j_end;
-        if (more) {
-            stage(jj + 1, buf ^ 1);
-            load_k(jj + 1, knext);
-        }
-        const __bf16* dST = reinterpret_cast<const __bf16*>(smem + buf * DS_B);
+    stage(0, 0);
+    load_k(0, kb[0]);
+    auto step = [&](int jj, auto stI) {
+        constexpr int st = decltype(stI)::value;
+        vm_wait<0>(kb[st]);
+        __builtin_amdgcn_s_barrier();           // step jj landed for every wave; the other stage is free
+        stage(min(jj + 1, j_end - 1), st ^ 1);
+        load_k(min(jj + 1, j_end - 1), kb[st ^ 1]);
+        if (jj >= j_end) return;
+        // A operands: transposing reads issued from assembly two k steps
+        // ahead (the compiler would wait for every tile copy in flight
+        // before its own), 2 TQ reads per k step
+        u32x2 ta[KS][TQ][2];
+        auto issue = [&](auto ksI) {
+            constexpr int ks = decltype(ksI)::value;
+            constexpr int off = st * STB + 256 * (ks & 1) + 2048 * ((ks >> 1) & 1) + 4096 * (ks >> 2);
 #pragma unroll
-        for (int ks = 0; ks < BC / 16; ++ks) {
-#pragma unroll
-            for (int t = 0; t < TQ; ++t) {
-                const int kso = (256 * (ks & 1) + 2048 * ((ks >> 1) & 1) + 4096 * (ks >> 2)) / 2;
-                const bf16x8 a = cat44(lds_read_tr(dST + ods[t][0] + kso), lds_read_tr(dST + ods[t][1] + kso));
-                acc[t] = mfma32(a, kcur[ks], acc[t]);
-            }
-        }
-        __syncthreads();                        // next tile landed; this buffer free
-        if (more) {
-#pragma unroll
-            for (int ks = 0; ks < BC / 16; ++ks) kcur[ks] = knext[ks];
-        }
+            for (int t = 0; t < TQ; ++t) tr_read2o<off>(ta[ks][t][0], ta[ks][t][1], tra[t][0], tra[t][1]);
+        };
+        issue(std::integral_constant<int, 0>{});
+        issue(std::integral_constant<int, 1>{});
+        static_for<0, KS>([&](auto ksI) {
+            constexpr int ks = decltype(ksI)::value;
+            if constexpr (ks + 2 < KS) issue(std::integral_constant<int, ks + 2>{});
+            constexpr int later = (ks + 2 < KS ? 2 : KS - 1 - ks) * 2 * TQ;
+            static_for<0, TQ>([&](auto tI) {
+                constexpr int t = decltype(tI)::value;
+                lgkm_wait<later + 2 * (TQ - 1 - t)>(ta[ks][t][0], ta[ks][t][1]);
+                acc[t] = mfma32(cat_u(ta[ks][t][0], ta[ks][t][1]), kb[st][ks], acc[t]);
+            });
+        });
+    };
+    for (int jj = 0; jj < j_end; jj += NST) {
+        step(jj, std::integral_constant<int, 0>{});
+        step(jj + 1, std::integral_constant<int, 1>{});
     }
+    vm_wait<0>(kb[0]);                           // no copy into LDS outlives the workgroup
 
     // ---- dQ = scale * acc, bf16 (RNE); rows past the end are not stored
     __bf16* dQh = dQ + (size_t)bh * N * HD;
@@ -1200,7 +1269,7 @@ template <int HD, bool CAUSAL>
 static hipError_t launch_dq(const __bf16* kimg, const __bf16* dSw, void* dq, int BH, int N,
                             float scale, hipStream_t stream) {
     const int tr = (N + bwd::BR - 1) / bwd::BR;
-    hipLaunchKernelGGL((bwd::bwd_dq_kernel<HD, CAUSAL>), dim3(BH * tr), dim3(bwd::QW * 64), 0, stream,
+    hipLaunchKernelGGL((bwd::bwd_dq_kernel<HD, CAUSAL>), dim3(BH * ((tr + 1) / 2)), dim3(bwd::QW * 64), 0, stream,
                        kimg, dSw, (__bf16*)dq, BH, N, scale);
     return hipGetLastError();
 }
