@@ -634,17 +634,18 @@ __device__ __forceinline__ void vm_wait(bf16x8* r) {
 // Issue order of the LDS reads of one 32-row half of the d = 128 dK/dV
 // kernel, so that every wait is exact.  A half starts with L row group 0 and
 // the 8 Q steps of S in flight (reads 0 .. 8); then per slot: S phase slot ks
-// reads the dP operands of step ks - 5 (dO, V block 0, V block 1); dP slot m
-// reads the transposed dO of dV steps 0 / 1 (m = 12 / 14), the dP operands of
-// step m / 2 + 3 (even m up to 8), L group m / 4 + 1 (m = 0, 4, 8) and D
+// reads the dP operands of step ks - (8 - PD) (dO, V block 0, V block 1); dP
+// slot m reads the transposed dO of dV steps 0 / 1 (m = 12 / 14), the dP
+// operands of step m / 2 + PD (even m), L group m / 4 + 1 (m = 0, 4, 8) and D
 // groups 0 / 1 (m = 9 / 11); dV slot m reads D group m / 4 + 2 (m = 0, 4),
 // then (even m) the transposed reads of dV step m / 2 + 2 or dK step
 // m / 2 - 6; dK slot m (even, m < 12) the transposed Q of dK step m / 2 + 2.
 struct W64Sched {
     static constexpr int KS = 8;
-    static constexpr int S_LD(int ks) { return ks >= KS - 3 ? 3 : 0; }
+    static constexpr int PD = 4;                 // k steps of dP operands read ahead
+    static constexpr int S_LD(int ks) { return ks >= KS - PD ? 3 : 0; }
     static constexpr int P_TR(int m) { return (m == 12 || m == 14) ? 2 : 0; }
-    static constexpr int P_DP(int m) { return (m % 2 == 0 && m / 2 + 3 < KS) ? 3 : 0; }
+    static constexpr int P_DP(int m) { return (m % 2 == 0 && m / 2 + PD < KS) ? 3 : 0; }
     static constexpr int P_LV(int m) { return (m % 4 == 0 && m < 12) ? 1 : 0; }
     static constexpr int P_DD(int m) { return (m == 9 || m == 11) ? 1 : 0; }
     static constexpr int P_LD(int m) { return P_TR(m) + P_DP(m) + P_LV(m) + P_DD(m); }
@@ -678,7 +679,7 @@ struct W64Sched {
         return rr == 0 ? 0 : P_end(4 * (rr - 1) - 1) + P_TR(4 * (rr - 1)) + P_DP(4 * (rr - 1));
     }
     static constexpr int i_ado(int ks) {
-        return ks < 3 ? S_end(ks + KS - 3 - 1) : P_end(2 * (ks - 3) - 1) + P_TR(2 * (ks - 3));
+        return ks < PD ? S_end(ks + KS - PD - 1) : P_end(2 * (ks - PD) - 1) + P_TR(2 * (ks - PD));
     }
     static constexpr int i_bv(int ks, int kb) { return i_ado(ks) + 1 + kb; }
     static constexpr int i_dd(int rr) { return rr < 2 ? P_end(9 + 2 * rr - 1) : V_end(4 * (rr - 2) - 1); }
@@ -923,7 +924,7 @@ void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict_
                     if constexpr (ks == 0) mfma_v0(s[kb], aq[ks], kreg[kb][ks]);
                     else mfma_v(s[kb], aq[ks], kreg[kb][ks]);
                 });
-                if constexpr (SC::S_LD(ks) > 0) load_dp(std::integral_constant<int, ks - (KSD - 3)>{});
+                if constexpr (SC::S_LD(ks) > 0) load_dp(std::integral_constant<int, ks - (KSD - SC::PD)>{});
                 __builtin_amdgcn_sched_barrier(0);
             });
             mfma_v_settle2(s[0], s[1]);
@@ -951,7 +952,7 @@ void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict_
                 constexpr int m = decltype(mI)::value, ks = m >> 1, kb = m & 1, rr = m >> 2;
                 if constexpr (m == 12) tr_step(std::integral_constant<int, 0>{}, IsDo{});
                 if constexpr (m == 14) tr_step(std::integral_constant<int, 1>{}, IsDo{});
-                if constexpr (SC::P_DP(m) > 0) load_dp(std::integral_constant<int, ks + 3>{});
+                if constexpr (SC::P_DP(m) > 0) load_dp(std::integral_constant<int, ks + SC::PD>{});
                 if constexpr (SC::P_LV(m) > 0) lds_ld<qb * 128 + (rr + 1) * 32>(lv[rr + 1], aL);
                 if constexpr (SC::P_DD(m) > 0) load_dd(std::integral_constant<int, ((m - 9) >> 1)>{});
                 // each register is tied to the first wait that covers it only
