@@ -44,6 +44,7 @@
 
 #include "common.hpp"
 #include "launch.hpp"
+#include "w64_sched.hpp"
 
 namespace attn {
 
@@ -611,8 +612,6 @@ __device__ __forceinline__ void lgkm_wait(A& a, B& b, C& c) {
     asm volatile("s_waitcnt lgkmcnt(%[n])" : "+v"(a), "+v"(b), "+v"(c) : [n] "n"(N > 15 ? 15 : N));
 }
 
-constexpr int cmax(int a, int b) { return a > b ? a : b; }
-
 // 16-byte global load at base + voff + OFF (OFF < 4096), issued where it
 // stands; vm_wait must follow before the result is used.
 template <int OFF>
@@ -630,66 +629,6 @@ __device__ __forceinline__ void vm_wait(bf16x8* r) {
                  : [n] "n"(N)
                  : "memory");
 }
-
-// Issue order of the LDS reads of one 32-row half of the d = 128 dK/dV
-// kernel, so that every wait is exact.  A half starts with L row group 0 and
-// the 8 Q steps of S in flight (reads 0 .. 8); then per slot: S phase slot ks
-// reads the dP operands of step ks - (8 - PD) (dO, V block 0, V block 1); dP
-// slot m reads the transposed dO of dV steps 0 / 1 (m = 12 / 14), the dP
-// operands of step m / 2 + PD (even m), L group m / 4 + 1 (m = 0, 4, 8) and D
-// groups 0 / 1 (m = 9 / 11); dV slot m reads D group m / 4 + 2 (m = 0, 4),
-// then (even m) the transposed reads of dV step m / 2 + 2 or dK step
-// m / 2 - 6; dK slot m (even, m < 12) the transposed Q of dK step m / 2 + 2.
-struct W64Sched {
-    static constexpr int KS = 8;
-    static constexpr int PD = 4;                 // k steps of dP operands read ahead
-    static constexpr int S_LD(int ks) { return ks >= KS - PD ? 3 : 0; }
-    static constexpr int P_TR(int m) { return (m == 12 || m == 14) ? 2 : 0; }
-    static constexpr int P_DP(int m) { return (m % 2 == 0 && m / 2 + PD < KS) ? 3 : 0; }
-    static constexpr int P_LV(int m) { return (m % 4 == 0 && m < 12) ? 1 : 0; }
-    static constexpr int P_DD(int m) { return (m == 9 || m == 11) ? 1 : 0; }
-    static constexpr int P_LD(int m) { return P_TR(m) + P_DP(m) + P_LV(m) + P_DD(m); }
-    static constexpr int V_DD(int m) { return (m == 0 || m == 4) ? 1 : 0; }
-    static constexpr int V_LD(int m) { return V_DD(m) + (m % 2 == 0 ? 2 : 0); }
-    static constexpr int K_LD(int m) { return (m % 2 == 0 && m / 2 + 2 < 8) ? 2 : 0; }
-    // reads issued up to and including slot ks / m of each phase
-    static constexpr int S_end(int ks) {
-        int n = 1 + KS;
-        for (int k = 0; k <= ks; ++k) n += S_LD(k);
-        return n;
-    }
-    static constexpr int P_end(int m) {
-        int n = S_end(KS - 1);
-        for (int i = 0; i <= m; ++i) n += P_LD(i);
-        return n;
-    }
-    static constexpr int V_end(int m) {
-        int n = P_end(15);
-        for (int i = 0; i <= m; ++i) n += V_LD(i);
-        return n;
-    }
-    static constexpr int K_end(int m) {
-        int n = V_end(15);
-        for (int i = 0; i <= m; ++i) n += K_LD(i);
-        return n;
-    }
-    // position of each read in the sequence (the later read of a pair)
-    static constexpr int i_aq(int ks) { return 1 + ks; }
-    static constexpr int i_lv(int rr) {
-        return rr == 0 ? 0 : P_end(4 * (rr - 1) - 1) + P_TR(4 * (rr - 1)) + P_DP(4 * (rr - 1));
-    }
-    static constexpr int i_ado(int ks) {
-        return ks < PD ? S_end(ks + KS - PD - 1) : P_end(2 * (ks - PD) - 1) + P_TR(2 * (ks - PD));
-    }
-    static constexpr int i_bv(int ks, int kb) { return i_ado(ks) + 1 + kb; }
-    static constexpr int i_dd(int rr) { return rr < 2 ? P_end(9 + 2 * rr - 1) : V_end(4 * (rr - 2) - 1); }
-    static constexpr int i_trv(int t) {
-        return (t == 0 ? P_end(11) : t == 1 ? P_end(13) : V_end(2 * (t - 2) - 1) + V_DD(2 * (t - 2))) + 1;
-    }
-    static constexpr int i_trk(int t) {
-        return (t < 2 ? V_end(2 * (t + 6) - 1) + V_DD(2 * (t + 6)) : K_end(2 * (t - 2) - 1)) + 1;
-    }
-};
 
 template <int PENDING>
 __device__ __forceinline__ void tr_wait(u32x2& a, u32x2& b, u32x2& c, u32x2& d) {
@@ -918,7 +857,7 @@ void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict_
             // ---- S = Q K^T: 32 queries x 64 keys
             static_for<0, KSD>([&](auto ksI) {
                 constexpr int ks = decltype(ksI)::value;
-                lgkm_wait<SC::S_end(ks - 1) - 1 - SC::i_aq(ks)>(aq[ks]);
+                lgkm_wait<SC::wait_S(ks)>(aq[ks]);
                 static_for<0, 2>([&](auto kbI) {
                     constexpr int kb = decltype(kbI)::value;
                     if constexpr (ks == 0) mfma_v0(s[kb], aq[ks], kreg[kb][ks]);
@@ -957,11 +896,11 @@ void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict_
                 if constexpr (SC::P_DD(m) > 0) load_dd(std::integral_constant<int, ((m - 9) >> 1)>{});
                 // each register is tied to the first wait that covers it only
                 if constexpr (kb == 1)
-                    lgkm_wait<SC::P_end(m) - 1 - SC::i_bv(ks, 1)>(bv[ks][1]);
+                    lgkm_wait<SC::wait_P(m)>(bv[ks][1]);
                 else if constexpr ((m & 3) == 0)
-                    lgkm_wait<SC::P_end(m) - 1 - cmax(SC::i_bv(ks, 0), SC::i_lv(rr))>(ado[ks], bv[ks][0], lv[rr]);
+                    lgkm_wait<SC::wait_P(m)>(ado[ks], bv[ks][0], lv[rr]);
                 else
-                    lgkm_wait<SC::P_end(m) - 1 - SC::i_bv(ks, 0)>(ado[ks], bv[ks][0]);
+                    lgkm_wait<SC::wait_P(m)>(ado[ks], bv[ks][0]);
                 if constexpr (ks == 0) mfma_v0(dp[kb], ado[ks], bv[ks][kb]);
                 else mfma_v(dp[kb], ado[ks], bv[ks][kb]);
                 constexpr int ekb = (m >> 1) & 1;
@@ -986,9 +925,9 @@ void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict_
                     else tr_step(std::integral_constant<int, t - 6>{}, IsQ{});
                 }
                 if constexpr ((m & 3) == 0)
-                    lgkm_wait<SC::V_end(m) - 1 - cmax(SC::i_trv(t), SC::i_dd(rr))>(tb[t][0], tb[t][1], dd[rr]);
+                    lgkm_wait<SC::wait_V(m)>(tb[t][0], tb[t][1], dd[rr]);
                 else if constexpr (kb == 0)
-                    lgkm_wait<SC::V_end(m) - 1 - SC::i_trv(t)>(tb[t][0], tb[t][1]);
+                    lgkm_wait<SC::wait_V(m)>(tb[t][0], tb[t][1]);
                 if constexpr (m == 0 || m == 1) pa[m][1] = pack_c8(s[m], 8);
                 mfma_a(dv[kb][t & 3], pa[kb][t >> 2], cat_u(tb[t][0], tb[t][1]));
                 constexpr int ekb = (m >> 1) & 1;
@@ -1004,7 +943,7 @@ void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict_
             static_for<0, 16>([&](auto mI) {
                 constexpr int m = decltype(mI)::value, t = m >> 1, kb = m & 1;
                 if constexpr (SC::K_LD(m) > 0) tr_step(std::integral_constant<int, t + 2>{}, IsQ{});
-                if constexpr (kb == 0) lgkm_wait<SC::K_end(m) - 1 - SC::i_trk(t)>(tb[t][0], tb[t][1]);
+                if constexpr (kb == 0) lgkm_wait<SC::wait_K(m)>(tb[t][0], tb[t][1]);
                 if constexpr (m == 0 || m == 1) da[m][1] = pack_c8(dp[m], 8);
                 if constexpr (m >= 2 && m < 6) {
                     // run (sk, k4) = (0, 0) (1, 0) (0, 1) (1, 1) of this wave's block
