@@ -86,6 +86,10 @@ RAGGED = [
     DenseConfig("one_row_n", 2, 1, 1, 64, False, seed=6),
     DenseConfig("tile_plus1", 1, 1, 129, 128, True, seed=7),
     DenseConfig("tile_minus1", 1, 1, 255, 64, False, seed=8),
+    # B*H a multiple of 16: the causal dK/dV kernel's head-pair dispatch, with
+    # an odd number of 64-row query tiles (the dQ kernel's last pair has one)
+    DenseConfig("heads16_c128", 1, 16, 300, 128, True, seed=9),
+    DenseConfig("heads32_c64", 2, 16, 200, 64, True, seed=10),
 ]
 
 
