@@ -42,8 +42,10 @@
 //    register-ready image of K_j that the dK/dV kernel writes once per tile.
 #include <type_traits>
 
+#include "asm_ops.hpp"
 #include "common.hpp"
 #include "launch.hpp"
+#include "tiles.hpp"
 #include "w64_sched.hpp"
 
 namespace attn {
@@ -104,32 +106,6 @@ constexpr int BR = 64;           // query rows per iteration
 constexpr int NW = 8;            // wave64s per workgroup (2 per SIMD)
 constexpr int NT = NW * 64;
 
-// LDS tiles (all unpadded).  gfx950's LDS serves a 16-byte read for 16 lanes
-// per clock across 64 banks, i.e. one 256-byte bank line.
-//  * row-major [rows][HD] tiles (Q_i, dO_i, K_j, V_j): the 16-byte chunk c of
-//    row r lives at chunk c ^ rswz<HD>(r).  For HD = 128 (one row per bank
-//    line) rswz takes 16 distinct values on any 16 consecutive rows, so the
-//    16-byte operand reads of 16 consecutive rows are conflict-free; its bits
-//    2..3 are r & 3, so the 4 rows x 4 chunks of one transposing read also land
-//    on 16 distinct chunks.  For HD = 64 (two rows per bank line) the same two
-//    properties hold per row parity.
-//  * dS tiles in the dQ kernel: see dst_lds_chunk.
-template <int HD>
-__device__ __forceinline__ int rswz(int r) {
-    return HD == 128 ? (((r & 3) << 2) | ((r >> 2) & 3))
-                     : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
-}
-
-template <int HD>
-__device__ __forceinline__ int roff(int r, int c) {      // chunk c of row r (elements)
-    return r * HD + ((c ^ rswz<HD>(r)) << 3);
-}
-
-template <int HD>
-__device__ __forceinline__ int roff4(int r, int col) {   // 4 elements at col (multiple of 4)
-    return r * HD + ((((col >> 3) ^ rswz<HD>(r))) << 3) + (col & 4);
-}
-
 template <int HD> struct Smem {
     static constexpr int TILE = BR * HD * 2;              // one Q_i or dO_i tile (bytes)
     static constexpr int off_q = 0;                       // two buffers
@@ -143,62 +119,6 @@ template <int HD> struct Smem {
     static constexpr int xchg = 4 * 2 * (HD / 32) * 16 * 64 * 4;
     static_assert(xchg <= off_l, "partial exchange must fit below L / D");
 };
-
-// Copy ROWS rows of a [*, HD] bf16 tensor, starting at the descriptor's base,
-// into a swizzled LDS tile with WAVES waves (rows past the descriptor's end
-// arrive as zeros, whose contributions are masked).  voff[i] are the per-lane
-// byte offsets of instruction i (see stage_offsets).
-template <int HD, int ROWS, int WAVES>
-__device__ __forceinline__ void stage_rows_b(__amdgpu_buffer_rsrc_t r, const int* voff, char* tile,
-                                             int w) {
-    constexpr int IPW = ROWS * (HD / 8) / 64 / WAVES;
-#pragma unroll
-    for (int i = 0; i < IPW; ++i) bdma16(r, voff[i], tile + (w * IPW + i) * 1024);
-}
-
-// Copy rows [row0, row0 + ROWS) of a [*, HD] bf16 tensor into a swizzled LDS
-// tile with WAVES waves; rows at or past N re-read row N - 1 (finite values
-// whose contributions are masked to zero).
-template <int HD, int ROWS, int WAVES>
-__device__ __forceinline__ void stage_rows(const __bf16* src, int row0, int N, char* tile, int w,
-                                           int lane) {
-    constexpr int CPR = HD / 8;
-    constexpr int IPW = ROWS * CPR / 64 / WAVES;          // instructions per wave
-#pragma unroll
-    for (int i = 0; i < IPW; ++i) {
-        const int I = w * IPW + i;
-        const int P = I * 64 + lane;                       // physical chunk
-        const int r = P / CPR;
-        const int c = (P % CPR) ^ rswz<HD>(r);             // logical chunk stored there
-        const int row = min(row0 + r, N - 1);
-        dma16(src + (size_t)row * HD + c * 8, tile + I * 1024);
-    }
-}
-
-// Per-lane source byte offsets for stage_rows_b: the physical chunk this lane
-// writes belongs to row r, logical chunk (p ^ rswz(r)).
-template <int HD, int ROWS, int WAVES>
-__device__ __forceinline__ void stage_offsets(int* voff, int w, int lane) {
-    constexpr int CPR = HD / 8;
-    constexpr int IPW = ROWS * CPR / 64 / WAVES;
-#pragma unroll
-    for (int i = 0; i < IPW; ++i) {
-        const int P = (w * IPW + i) * 64 + lane;
-        const int r = P / CPR;
-        voff[i] = (r * HD + (((P % CPR) ^ rswz<HD>(r)) << 3)) * 2;
-    }
-}
-
-// Copy BYTES contiguous bytes (a multiple of WAVES * 1024) into LDS.
-template <int BYTES, int WAVES>
-__device__ __forceinline__ void stage_bytes(const char* src, char* dst, int w, int lane) {
-    constexpr int IPW = BYTES / 1024 / WAVES;
-#pragma unroll
-    for (int i = 0; i < IPW; ++i) {
-        const int I = w * IPW + i;
-        dma16(src + I * 1024 + lane * 16, dst + I * 1024);
-    }
-}
 
 // Workspace tile of dS for one (batch*head, query tile i, 128-key tile j),
 // BC x BR bf16 = 16 KiB, in the register order of its producer so that every
@@ -492,156 +412,6 @@ struct Smem2 {
     static constexpr int off_kstage = 0;                  // K_j in the prologue (overlays Q/dO)
     static_assert(BC2 * HD * 2 <= off_v, "K staging must fit below V");
 };
-
-// Compile-time loop: f(std::integral_constant<int, i>) for i = I .. N-1, so
-// that indices are constants (immediate offsets, if constexpr).
-template <int I, int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-    if constexpr (I < N) {
-        f(std::integral_constant<int, I>{});
-        static_for<I + 1, N>(f);
-    }
-}
-
-// The S / dP products of this kernel are issued as VGPR-form MFMAs: with the
-// 256 dK / dV accumulator registers in the AGPR file, leaving the choice to the
-// compiler puts every MFMA result in AGPRs and overflows them.  Hazards this
-// implies (the compiler inserts them for its own MFMAs): a VALU read of an
-// MFMA result needs 12 wait states after the MFMA (mfma_v_settle gives 16),
-// dependent accumulation and LDS loads into the operand registers need none.
-__device__ __forceinline__ void mfma_v(f32x16& c, const bf16x8& a, const bf16x8& b) {
-    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
-}
-
-__device__ __forceinline__ void mfma_v0(f32x16& c, const bf16x8& a, const bf16x8& b) {
-    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(c) : "v"(a), "v"(b));
-}
-
-__device__ __forceinline__ void mfma_v_settle2(f32x16& a, f32x16& b) {
-    asm volatile("s_nop 15" : "+v"(a), "+v"(b));
-}
-
-// dV / dK accumulation into the AGPR file; no VALU reads these registers
-// until acc_settle after the last one.
-__device__ __forceinline__ void mfma_a(f32x16& c, const bf16x8& a, const bf16x8& b) {
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
-}
-
-// Transposing LDS reads issued from inline assembly.  The compiler treats its
-// own ds_read_b64_tr_b16 as possibly reading what an in-flight buffer -> LDS
-// copy writes and waits for all of them (vmcnt(0)) first, which would expose
-// the next tile's copy latency in every iteration; these reads only touch the
-// current tile, which the copies never write.  The compiler does not track
-// their completion, so tr_wait must follow before the results are used: with
-// `pending` = the number of LDS reads issued after them, lgkmcnt(pending)
-// guarantees they are done (LDS operations complete in order).
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return (uint32_t)reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p);
-}
-
-__device__ __forceinline__ void tr_read4(u32x2& a, u32x2& b, u32x2& c, u32x2& d, uint32_t pa,
-                                         uint32_t pb, uint32_t pc, uint32_t pd) {
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %4\n\t"
-        "ds_read_b64_tr_b16 %1, %5\n\t"
-        "ds_read_b64_tr_b16 %2, %6\n\t"
-        "ds_read_b64_tr_b16 %3, %7"
-        : "=&v"(a), "=&v"(b), "=&v"(c), "=&v"(d)
-        : "v"(pa), "v"(pb), "v"(pc), "v"(pd));
-}
-
-__device__ __forceinline__ void tr_read2(u32x2& a, u32x2& b, uint32_t pa, uint32_t pb) {
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %2\n\t"
-        "ds_read_b64_tr_b16 %1, %3"
-        : "=&v"(a), "=&v"(b)
-        : "v"(pa), "v"(pb));
-}
-
-template <int OFF>
-__device__ __forceinline__ void tr_read2o(u32x2& a, u32x2& b, uint32_t pa, uint32_t pb) {
-    static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %2 offset:%4\n\t"
-        "ds_read_b64_tr_b16 %1, %3 offset:%4"
-        : "=&v"(a), "=&v"(b)
-        : "v"(pa), "v"(pb), "n"(OFF));
-}
-
-template <int PENDING>
-__device__ __forceinline__ void tr_wait2(u32x2& a, u32x2& b) {
-    static_assert(PENDING >= 0 && PENDING <= 15, "pending count");
-    asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(PENDING));
-}
-
-// 16-byte LDS read at a + OFF, issued where it stands; lgkm_wait must follow
-// before the result is used.
-template <int OFF, typename T>
-__device__ __forceinline__ void lds_ld(T& d, uint32_t a) {
-    static_assert(sizeof(T) == 16 && OFF >= 0 && OFF < 65536, "b128 read");
-    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=&v"(d) : "v"(a), "n"(OFF));
-}
-
-// a ^ C, computed where it stands (C = 0: a itself)
-template <int C>
-__device__ __forceinline__ uint32_t vxor(uint32_t a) {
-    if constexpr (C == 0) {
-        return a;
-    } else {
-        uint32_t r;
-        asm volatile("v_xor_b32 %0, %1, %2" : "=v"(r) : "n"(C), "v"(a));
-        return r;
-    }
-}
-
-// s_waitcnt lgkmcnt(N) (N above 15 waits for 15, which is stricter), tied to
-// the registers whose loads it completes
-template <int N, typename A>
-__device__ __forceinline__ void lgkm_wait(A& a) {
-    static_assert(N >= 0, "wait count");
-    asm volatile("s_waitcnt lgkmcnt(%[n])" : "+v"(a) : [n] "n"(N > 15 ? 15 : N));
-}
-template <int N, typename A, typename B>
-__device__ __forceinline__ void lgkm_wait(A& a, B& b) {
-    static_assert(N >= 0, "wait count");
-    asm volatile("s_waitcnt lgkmcnt(%[n])" : "+v"(a), "+v"(b) : [n] "n"(N > 15 ? 15 : N));
-}
-template <int N, typename A, typename B, typename C>
-__device__ __forceinline__ void lgkm_wait(A& a, B& b, C& c) {
-    static_assert(N >= 0, "wait count");
-    asm volatile("s_waitcnt lgkmcnt(%[n])" : "+v"(a), "+v"(b), "+v"(c) : [n] "n"(N > 15 ? 15 : N));
-}
-
-// 16-byte global load at base + voff + OFF (OFF < 4096), issued where it
-// stands; vm_wait must follow before the result is used.
-template <int OFF>
-__device__ __forceinline__ void gload16(bf16x8& d, const void* base, uint32_t voff) {
-    static_assert(OFF >= 0 && OFF < 4096, "global offset field");
-    asm volatile("global_load_dwordx4 %0, %1, %2 offset:%3" : "=&v"(d) : "v"(voff), "s"(base), "n"(OFF));
-}
-
-// s_waitcnt vmcnt(N), tied to the eight registers whose loads it completes
-template <int N>
-__device__ __forceinline__ void vm_wait(bf16x8* r) {
-    static_assert(N >= 0 && N < 64, "vmcnt");
-    asm volatile("s_waitcnt vmcnt(%[n])"
-                 : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]), "+v"(r[6]), "+v"(r[7])
-                 : [n] "n"(N)
-                 : "memory");
-}
-
-template <int PENDING>
-__device__ __forceinline__ void tr_wait(u32x2& a, u32x2& b, u32x2& c, u32x2& d) {
-    static_assert(PENDING == 0 || PENDING == 4, "pending count");
-    if (PENDING == 0)
-        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
-    else
-        asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
-}
-
-__device__ __forceinline__ bf16x8 cat_u(u32x2 lo, u32x2 hi) {
-    return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-}
 
 template <bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW2 * 64, NW2 * 64), amdgpu_waves_per_eu(1, 1)))

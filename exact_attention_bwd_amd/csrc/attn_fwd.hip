@@ -20,8 +20,13 @@
 //  * O^T = V^T P^T: P^T (B operand) comes straight from the S^T accumulators;
 //    V^T (A operand) is staged transposed and XOR-swizzled in LDS.
 //  * The next K/V tile is fetched into registers during the current one.
+#include <type_traits>
+
+#include "asm_ops.hpp"
 #include "common.hpp"
+#include "fwd_sched.hpp"
 #include "launch.hpp"
+#include "tiles.hpp"
 
 namespace attn {
 namespace fwd {
@@ -241,6 +246,448 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     }
 }
 
+
+// ----------------------------------------------------------------------------
+// d = 128: fwd_w64_kernel.  One workgroup of 4 wave64s (one per SIMD) per
+// 256-row query tile; wave w owns rows 64 w .. + 63 as two 32-row blocks qb.
+//
+//  * Every K or V^T operand read from LDS feeds two MFMAs (one per row
+//    block), which halves the LDS traffic per product against 32 rows per
+//    wave.  Q (the B operand of S^T = K Q^T) stays in the AGPR file for the
+//    whole loop, next to the O^T accumulators.
+//  * K and V tiles of 64 keys arrive by direct buffer -> LDS copies into a
+//    ring of 2 K slots and 3 V slots; one barrier per tile orders the copies
+//    against the reads (see the slot rules at the loop).
+//  * Software pipeline over key tiles t: iteration t runs the S phase (the
+//    32 MFMAs of S(t+1) = K_{t+1} Q^T, with the exponentials of tile t's
+//    second key block on the VALU) and then the PV phase (the 32 MFMAs of
+//    O^T += V_t^T P_t^T, with the row max of S(t+1) and the exponentials of
+//    its first key block on the VALU).  Each MFMA slot ends in a
+//    sched_barrier that keeps the compiler from regrouping the work.
+//  * Online softmax with a lazy rescale (B200 attention blog, Chapter 8,
+//    conditional rescaling): the exponent offset m of a row only moves when
+//    the running max exceeds it by more than 8 (log2 units), so
+//    P = 2^(S scale log2 e - m) <= 256 and O and l are rescaled by
+//    2^(m_old - m_new) only then (a wave-uniform branch, taken only by waves
+//    with such a row).
+//  * Every LDS read is issued from assembly at a fixed point and waited for
+//    with the count FwdSched derives from the issue order.
+// ----------------------------------------------------------------------------
+constexpr int WBM = 256;                 // query rows per workgroup
+constexpr int WNW = 4;                   // wave64s per workgroup
+
+struct WSmem {
+    static constexpr int TILE = BN * 128 * 2;        // one K or V tile: 16 KiB
+    static constexpr int off_k = 0;                  // K slots 0, 1
+    static constexpr int off_v = 2 * TILE;           // V slots 0, 1, 2
+    static constexpr int bytes = 5 * TILE;
+};
+
+// S^T products: result in VGPRs (the VALU reads it); the K and Q operands
+// come from AGPRs
+__device__ __forceinline__ void mfma_q(f32x16& c, const bf16x8& a, const bf16x8& b) {
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "a"(a), "a"(b));
+}
+
+__device__ __forceinline__ void mfma_q0(f32x16& c, const bf16x8& a, const bf16x8& b) {
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(c) : "a"(a), "a"(b));
+}
+
+// O^T accumulation: V^T and P^T operands from VGPRs, result in AGPRs
+__device__ __forceinline__ void mfma_o(f32x16& c, const bf16x8& a, const bf16x8& b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+
+// c += a0 b0 + a1 b1 with operands just written by the VALU: the wait states
+// before cover the VALU write -> MFMA operand read, those after keep the
+// compiler's next writes of these registers clear of the MFMAs' operand reads
+// (the compiler does not see MFMAs issued from assembly).
+__device__ __forceinline__ void mfma_mask(f32x16& c, const bf16x8& a0, const bf16x8& a1, const bf16x8& b0,
+                                          const bf16x8& b1) {
+    asm volatile(
+        "s_nop 4\n\t"
+        "v_mfma_f32_32x32x16_bf16 %0, %1, %3, %0\n\t"
+        "v_mfma_f32_32x32x16_bf16 %0, %2, %4, %0\n\t"
+        "s_nop 7"
+        : "+v"(c)
+        : "v"(a0), "v"(a1), "v"(b0), "v"(b1));
+}
+
+// x of lane l combined with x of lane l ^ 32: v_permlane32_swap exchanges the
+// upper half of one register with the lower half of another, so both halves
+// of a copy end up holding the other lane's value (no LDS involved)
+__device__ __forceinline__ float pair_max(float x) {
+    float y;
+    asm volatile(
+        "v_mov_b32 %1, %0\n\t"
+        "s_nop 1\n\t"
+        "v_permlane32_swap_b32 %0, %1\n\t"
+        "s_nop 1\n\t"
+        "v_max_f32 %0, %0, %1"
+        : "+v"(x), "=&v"(y));
+    return x;
+}
+
+__device__ __forceinline__ float pair_sum(float x) {
+    float y;
+    asm volatile(
+        "v_mov_b32 %1, %0\n\t"
+        "s_nop 1\n\t"
+        "v_permlane32_swap_b32 %0, %1\n\t"
+        "s_nop 1\n\t"
+        "v_add_f32 %0, %0, %1"
+        : "+v"(x), "=&v"(y));
+    return x;
+}
+
+template <bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(WNW * 64, WNW * 64), amdgpu_waves_per_eu(1, 1)))
+void fwd_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+                    const __bf16* __restrict__ V, __bf16* __restrict__ O, float* __restrict__ Lse,
+                    int BH, int N, float scale) {
+    constexpr int HD = 128;
+    using SC = FwdSched;
+    using S = WSmem;
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+
+    const int lane = threadIdx.x & 63;
+    const int w = wave_id();
+    const int l32 = lane & 31;
+    const int g = lane >> 5;
+    const int t16 = lane & 15;
+    const int hh = (lane >> 4) & 1;
+    const int s4 = t16 >> 2;
+
+    // Work order.  Causal: query tile qt sees 4 (qt + 1) key tiles, so the
+    // last tiles go first.  Workgroups are dealt round-robin over the 8 XCDs
+    // (hardware index b runs on XCD b % 8); each XCD takes every eighth head
+    // and works through them two at a time, longest tiles first within each
+    // pair, so that the few heads in flight on an XCD keep their K / V in its
+    // L2.  Other head counts: longest tiles first over all heads.
+    // Non-causal: the tiles of one head run on one XCD.
+    const int tq = (N + WBM - 1) / WBM;
+    int bh, qt;
+    if (CAUSAL && BH % 16 == 0) {
+        const int x = blockIdx.x % 8, t = blockIdx.x / 8;
+        const int grp = t / (2 * tq), r = t % (2 * tq);
+        qt = tq - 1 - r / 2;
+        bh = (2 * grp + (r & 1)) * 8 + x;
+    } else if (CAUSAL) {
+        bh = blockIdx.x % BH;
+        qt = tq - 1 - blockIdx.x / BH;
+    } else {
+        const int logical = xcd_remap(blockIdx.x, BH * tq);
+        bh = logical / tq;
+        qt = logical % tq;
+    }
+    const int q0 = qt * WBM;
+    const int qrows = min(N - q0, WBM);
+    const int qw = 64 * w;                       // this wave's first row in the tile
+    const size_t head = (size_t)bh * N * HD;
+    const __bf16* Kh = K + head;
+    const __bf16* Vh = V + head;
+    const int T = CAUSAL ? (q0 + qrows - 1) / BN + 1 : (N + BN - 1) / BN;   // key tiles
+
+    // Q rows of this lane as B operands of S^T: Q[qw + 32 qb + l32][16 ks + 8 g ..]
+    bf16x8 qa[2][8];
+    {
+        const __amdgpu_buffer_rsrc_t qr = make_rsrc(Q + head + (size_t)q0 * HD, qrows * HD * 2);
+        static_for<0, 2>([&](auto qbI) __attribute__((always_inline)) {
+            constexpr int qb = decltype(qbI)::value;
+            static_for<0, 8>([&](auto ksI) __attribute__((always_inline)) {
+                constexpr int ks = decltype(ksI)::value;
+                qa[qb][ks] = __builtin_bit_cast(
+                    bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qr, ((qw + 32 * qb + l32) * HD + 8 * g) * 2,
+                                                                  ks * 32, 0));
+            });
+        });
+    }
+
+    int voff[BN * (HD / 8) / 64 / WNW];
+    stage_offsets<HD, BN, WNW>(voff, w, lane);
+    // tiles at or past T (padding of the last iteration) are filled with zeros
+    auto dma = [&](const __bf16* base, int tile, int lds_off) __attribute__((always_inline)) {
+        const int n0 = tile * BN;
+        const int bytes = tile < T ? min(N - n0, BN) * HD * 2 : 0;
+        stage_rows_b<HD, BN, WNW>(make_rsrc(base + (size_t)min(n0, N - 1) * HD, bytes), voff, smem + lds_off, w);
+    };
+
+    // row reads of K: chunk 2 ks + g of row 32 kb + l32 at (aK ^ 32 ks) + 8 KiB kb
+    const uint32_t aK = lds_addr(smem) + (uint32_t)(roff<HD>(l32, g) * 2);
+    // transposing reads of V (A operand V^T): rows 4 g + s4 (+ 16 k4, + 8),
+    // columns 16 hh + 4 (t16 & 3) (+ 32 db); bases of the current V slot
+    const int otr = roff4<HD>(g * 4 + s4, hh * 16 + 4 * (t16 & 3));
+    uint32_t trv[4][2];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+        trv[db][0] = lds_addr(smem + S::off_v) + (uint32_t)((otr ^ (db << 5)) * 2);
+        trv[db][1] = lds_addr(smem + S::off_v) + (uint32_t)((((otr + 8 * HD) ^ (db << 5)) ^ 16) * 2);
+    }
+    // A operand of the mask product: ones where key l32 >= k (k = 16 h + 8 g + e)
+    bf16x8 tri[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) tri[h][e] = l32 >= 16 * h + 8 * g + e ? (__bf16)1.f : (__bf16)0.f;
+
+    f32x16 sa[2][2], sb[2][2];                   // S^T of tiles t (t even: sa) and t + 1
+    f32x16 o[2][4];                              // O^T, rows = head dim, in AGPRs
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) o[qb][db] = zero16();
+    u32x4 pk[2][4];                              // P^T operands (bf16 pairs)
+    bf16x8 kop[16];
+    u32x2 vop[16][2];
+    float mrow[2] = {-__builtin_inff(), -__builtin_inff()};   // exponent offset (log2 units)
+    float lrow[2] = {0.f, 0.f};                  // this lane's share of the normaliser
+    float oa[2] = {1.f, 1.f};                    // pending O rescale factor
+    float pmax[2];
+    bool pend[2] = {false, false};
+    const float sl2 = scale * kLog2e;
+
+    // operand j of an iteration whose K rows are in K slot KS
+    auto issue = [&](auto jI, auto ksI) __attribute__((always_inline)) {
+        constexpr int j = decltype(jI)::value, KS = decltype(ksI)::value;
+        if constexpr (j < 16) {
+            lds_ld_a<S::off_k + KS * S::TILE + (j >> 3) * 8192>(kop[j], vxor<(j & 7) * 32>(aK));
+        } else {
+            constexpr int v = j - 16;
+            tr_read2o<(v >> 2) * 4096>(vop[v][0], vop[v][1], trv[v & 3][0], trv[v & 3][1]);
+        }
+    };
+    float phold = 0.f;                           // first element of a pair
+    // element e (0 .. 63) of a tile's S^T: p = 2^(S scale log2 e - m), added to
+    // l and packed in pairs into the P^T operands.  e -> pair u = e / 2 of
+    // operand (row block qb, key step k4), k4 = u / 8, qb = (u / 4) % 2, dword
+    // i = u % 4, i.e. accumulator entry r = 8 (k4 % 2) + 2 i + e % 2 of key
+    // block k4 / 2.  Elements 0 .. 31 are key block 0, 32 .. 63 key block 1.
+    auto elem = [&](f32x16(&s)[2][2], auto eI, auto pinI) __attribute__((always_inline)) {
+        constexpr int e = decltype(eI)::value;
+        constexpr bool PIN = decltype(pinI)::value;
+        constexpr int u = e >> 1, jj = e & 1, k4 = u >> 3, qb = (u >> 2) & 1, i = u & 3;
+        constexpr int kb = k4 >> 1, r = 8 * (k4 & 1) + 2 * i + jj;
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][r], sl2, -mrow[qb]));
+        lrow[qb] += p;
+        // pinned in the loop: the compiler would otherwise sink the sums and
+        // packs towards their uses in the next iteration, past the rescale
+        // branch
+        if constexpr (PIN) asm volatile("" : "+v"(lrow[qb]));
+        if constexpr (jj == 0) {
+            phold = p;
+        } else {
+            typedef float f32x2 __attribute__((ext_vector_type(2)));
+            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+            pk[qb][k4][i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{phold, p}, bf16x2));
+            if constexpr (PIN) asm volatile("" : "+v"(pk[qb][k4]));
+        }
+    };
+    // Masking on the matrix core.  In block (qb, kb) of a tile, S^T entry
+    // (key k, row q) must become -inf when k > thr(q) = min(row, N - 1) - key
+    // offset.  With c(q) = clamp(thr(q) + 1, 0, 32), the product of the
+    // constant 32 x 32 matrix [k >= k'] (tri) and the matrix B[k'][q] = -2^120
+    // for k' = c(q), else 0, adds -2^120 exactly to the masked entries and 0 to
+    // the others; -2^120 scale log2 e underflows 2^x to 0 and never wins a
+    // row max.  Only blocks that reach past a row or past N take it (a
+    // wave-uniform branch around two MFMAs that update the block in place).
+    auto mask = [&](f32x16(&s)[2][2], auto qbI, auto kbI, int tile) __attribute__((always_inline)) {
+        constexpr int qb = decltype(qbI)::value, kb = decltype(kbI)::value;
+        const int kofs = tile * BN + 32 * kb;
+        const int qrow0 = q0 + qw + 32 * qb;
+        if ((CAUSAL && kofs + 31 > qrow0) || kofs + 31 > N - 1) {
+            const int lim = CAUSAL ? min(qrow0 + l32, N - 1) : N - 1;
+            const int c = min(max(lim - kofs + 1, 0), 32);
+            u32x4 bm[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int idx = c - 16 * h - 8 * g;    // element of this lane's operand that is hit
+#pragma unroll
+                for (int d = 0; d < 4; ++d)
+                    bm[h][d] = (idx >> 1) == d ? ((idx & 1) ? 0xFB800000u : 0x0000FB80u) : 0u;
+            }
+            mfma_mask(s[qb][kb], tri[0], tri[1], __builtin_bit_cast(bf16x8, bm[0]), __builtin_bit_cast(bf16x8, bm[1]));
+        }
+    };
+    auto max8 = [&](float m, const f32x16& s, int h) __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) m = __builtin_fmaxf(m, s[8 * h + r]);
+        return m;
+    };
+    // new offset of row block qb from its tile max pmax (this lane's keys)
+    auto combine = [&](int qb) __attribute__((always_inline)) {
+        const float mx = pair_max(pmax[qb]);
+        const float mn = __builtin_fmaxf(mrow[qb], mx * sl2);
+        const bool need = mn > mrow[qb] + 8.f;
+        const float alpha = __builtin_amdgcn_exp2f(mrow[qb] - mn);
+        mrow[qb] = need ? mn : mrow[qb];
+        lrow[qb] = need ? lrow[qb] * alpha : lrow[qb];
+        oa[qb] = need ? alpha : 1.f;
+        pend[qb] = __builtin_amdgcn_ballot_w64(need) != 0;
+    };
+
+    // ---- prologue: K_0, K_1, V_0; S(0); the first key block of tile 0
+    dma(Kh, 0, S::off_k);
+    dma(Kh, 1, S::off_k + S::TILE);
+    dma(Vh, 0, S::off_v);
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    static_for<0, SC::D>([&](auto jI) __attribute__((always_inline)) { issue(jI, I0{}); });
+    static_for<0, 32>([&](auto mI) __attribute__((always_inline)) {
+        constexpr int m = decltype(mI)::value, n = m >> 1, qb = m & 1, kb = n >> 3, ks = n & 7;
+        if constexpr (qb == 0) {
+            if constexpr (SC::issues(SC::PRO, n)) issue(std::integral_constant<int, n + SC::D>{}, I0{});
+            lgkm_wait_a<SC::wait(SC::PRO, n)>(kop[n]);
+        }
+        if constexpr (ks == 0) mfma_q0(sa[qb][kb], kop[n], qa[qb][ks]);
+        else mfma_q(sa[qb][kb], kop[n], qa[qb][ks]);
+        __builtin_amdgcn_sched_barrier(0);
+    });
+    // every wave has read K_0: its slot takes K_2; V_1 goes to V slot 1
+    asm volatile("s_barrier" ::: "memory");
+    dma(Kh, 2, S::off_k);
+    dma(Vh, 1, S::off_v + S::TILE);
+    static_for<0, SC::D>([&](auto jI) __attribute__((always_inline)) { issue(jI, I1{}); });   // K_1, iteration 0
+    static_for<0, 2>([&](auto qbI) __attribute__((always_inline)) {
+        mask(sa, qbI, I0{}, 0);
+        mask(sa, qbI, I1{}, 0);
+    });
+    mfma_v_settle2(sa[0][0], sa[0][1]);
+    mfma_v_settle2(sa[1][0], sa[1][1]);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+        pmax[qb] = max8(max8(max8(max8(-__builtin_inff(), sa[qb][0], 0), sa[qb][0], 1), sa[qb][1], 0), sa[qb][1], 1);
+    combine(0);
+    combine(1);
+    static_for<0, 32>([&](auto eI) __attribute__((always_inline)) { elem(sa, eI, std::false_type{}); });
+
+    // ---- main loop.  Slot rules (B_t = the barrier of iteration t):
+    //  * iteration t reads K_{t+1} (S phase; its first D operands are issued
+    //    after B_{t-1}) and V_t (from the S phase's need point 16 - D on);
+    //  * after B_t the wave copies K_{t+3} into the slot of K_{t+1} and
+    //    V_{t+2} into the slot of V_{t-1}; every wave finished those reads
+    //    before B_t, and each copy is complete (vmcnt(0)) and visible at
+    //    B_{t+1}, before its first read.
+    // The loop runs an even number of iterations; a padding tile T (zeros,
+    // every key masked) contributes nothing.
+    int vsl = 0;                                 // V slot of tile t: t % 3
+    auto iter = [&](auto pI, int t) __attribute__((always_inline)) {
+        constexpr int p = decltype(pI)::value;
+        constexpr int KS = p ^ 1;               // K slot of tile t + 1
+        f32x16(&sc)[2][2] = p ? sb : sa;         // tile t
+        f32x16(&sn)[2][2] = p ? sa : sb;         // tile t + 1
+        // ---- S phase: S(t+1); exponentials of tile t, key block 1
+        static_for<0, 32>([&](auto mI) __attribute__((always_inline)) {
+            constexpr int m = decltype(mI)::value, n = m >> 1, qb = m & 1, kb = n >> 3, ks = n & 7;
+            if constexpr (qb == 0) {
+                if constexpr (SC::issues(SC::ITER, n))
+                    issue(std::integral_constant<int, n + SC::D>{}, std::integral_constant<int, KS>{});
+                lgkm_wait_a<SC::wait(SC::ITER, n)>(kop[n]);
+            }
+            if constexpr (ks == 0) mfma_q0(sn[qb][kb], kop[n], qa[qb][ks]);
+            else mfma_q(sn[qb][kb], kop[n], qa[qb][ks]);
+            elem(sc, std::integral_constant<int, 32 + m>{}, std::true_type{});
+            // mask and row max of S(t+1), key block 0 (its last products: slots 14, 15)
+            if constexpr (m == 16) {
+                mask(sn, I0{}, I0{}, t + 1);
+                mask(sn, I1{}, I0{}, t + 1);
+                mfma_v_settle2(sn[0][0], sn[1][0]);
+            }
+            if constexpr (m >= 17 && m < 25) {
+                constexpr int b = (m - 17) >> 2, h = (m - 17) & 3;
+                if constexpr (h == 0) pmax[b] = -__builtin_inff();
+                pmax[b] = __builtin_fmaxf(pmax[b], __builtin_fmaxf(__builtin_fmaxf(sn[b][0][4 * h], sn[b][0][4 * h + 1]),
+                                                                   __builtin_fmaxf(sn[b][0][4 * h + 2], sn[b][0][4 * h + 3])));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        // ---- PV phase: O^T += V_t^T P_t^T; row max and key block 0 of tile t + 1
+        static_for<0, 32>([&](auto mI) __attribute__((always_inline)) {
+            constexpr int m = decltype(mI)::value, v = m >> 1, qb = m & 1, db = v & 3, k4 = v >> 2;
+            constexpr int n = 16 + v;
+            if constexpr (qb == 0) {
+                if constexpr (n == SC::BARRIER_N) {
+                    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+                    dma(Kh, t + 3, S::off_k + KS * S::TILE);
+                    dma(Vh, t + 2, S::off_v + (vsl == 0 ? 2 : vsl - 1) * S::TILE);
+                }
+                if constexpr (SC::issues(SC::ITER, n))
+                    issue(std::integral_constant<int, (n + SC::D) % SC::NOPS>{}, std::integral_constant<int, p>{});
+                lgkm_wait<SC::wait(SC::ITER, n)>(vop[v][0], vop[v][1]);
+            }
+            mfma_o(o[qb][db], cat_u(vop[v][0], vop[v][1]), __builtin_bit_cast(bf16x8, pk[qb][k4]));
+            if constexpr (m == 0) {
+                mask(sn, I0{}, I1{}, t + 1);
+                mask(sn, I1{}, I1{}, t + 1);
+                mfma_v_settle2(sn[0][1], sn[1][1]);      // last S(t+1) products: S slots 30, 31
+            }
+            if constexpr (m < 4) pmax[m >> 1] = max8(pmax[m >> 1], sn[m >> 1][1], m & 1);
+            if constexpr (m == 4) combine(0);
+            if constexpr (m == 5) combine(1);
+            if constexpr (m >= 8) {
+                constexpr int e0 = ((m - 8) * 4) / 3, e1 = ((m - 7) * 4) / 3;
+                static_for<e0, e1>([&](auto eI) __attribute__((always_inline)) { elem(sn, eI, std::true_type{}); });
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        // lazy rescale of O^T, after the last product that used the old offset
+        if (__builtin_expect(pend[0] || pend[1], 0)) {
+            asm volatile("s_nop 15\n\ts_nop 15"
+                         : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[0][2]), "+a"(o[0][3]),
+                           "+a"(o[1][0]), "+a"(o[1][1]), "+a"(o[1][2]), "+a"(o[1][3]));
+            static_for<0, 2>([&](auto qbI) __attribute__((always_inline)) {
+                constexpr int qb = decltype(qbI)::value;
+                if (pend[qb]) {
+                    static_for<0, 4>([&](auto dbI) __attribute__((always_inline)) {
+                        o[qb][decltype(dbI)::value] *= oa[qb];
+                        __builtin_amdgcn_sched_barrier(0);
+                    });
+                }
+            });
+        }
+        // V slot of tile t + 1
+        const int dv = vsl == 2 ? -2 * S::TILE : S::TILE;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+            trv[db][0] += dv;
+            trv[db][1] += dv;
+        }
+        vsl = vsl == 2 ? 0 : vsl + 1;
+    };
+    int t = 0;
+    do {                                         // T >= 1
+        iter(I0{}, t);
+        iter(I1{}, t + 1);
+        t += 2;
+    } while (t < T);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // copies issued for tiles past the end
+
+    // ---- O = O^T / l, L = (m + log2 l) ln 2
+    asm volatile("s_nop 15\n\ts_nop 15"
+                 : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[0][2]), "+a"(o[0][3]),
+                   "+a"(o[1][0]), "+a"(o[1][1]), "+a"(o[1][2]), "+a"(o[1][3]));
+    const __amdgpu_buffer_rsrc_t orc = make_rsrc(O + head + (size_t)q0 * HD, qrows * HD * 2);
+    static_for<0, 2>([&](auto qbI) __attribute__((always_inline)) {
+        constexpr int qb = decltype(qbI)::value;
+        const float lt = pair_sum(lrow[qb]);
+        const float inv = 1.f / lt;
+        const int row = qw + 32 * qb + l32;
+        static_for<0, 4>([&](auto dbI) __attribute__((always_inline)) {
+            constexpr int db = decltype(dbI)::value;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                bf16x4 v4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(o[qb][db][rr * 4 + e] * inv);
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v4), orc,
+                                                      (row * HD + db * 32 + rr * 8 + g * 4) * 2, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        if (g == 0 && row < qrows) Lse[(size_t)bh * N + q0 + row] = (mrow[qb] + __builtin_amdgcn_logf(lt)) * kLn2;
+    });
+}
+
 }  // namespace fwd
 
 template <int HD, bool CAUSAL>
@@ -254,12 +701,25 @@ static hipError_t launch_fwd_t(const void* q, const void* k, const void* v, void
     return hipGetLastError();
 }
 
+template <bool CAUSAL>
+static hipError_t launch_fwd_w64(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 int BH, int N, float scale, hipStream_t stream) {
+    using S = fwd::WSmem;
+    auto kern = fwd::fwd_w64_kernel<CAUSAL>;
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, S::bytes);
+    if (e != hipSuccess) return e;
+    const int tq = (N + fwd::WBM - 1) / fwd::WBM;
+    hipLaunchKernelGGL(kern, dim3(BH * tq), dim3(fwd::WNW * 64), S::bytes, stream, (const __bf16*)q,
+                       (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, BH, N, scale);
+    return hipGetLastError();
+}
+
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
                       int N, int d, bool causal, float scale, hipStream_t stream) {
     if ((long long)BH * N == 0) return hipSuccess;
     if (d == 128)
-        return causal ? launch_fwd_t<128, true>(q, k, v, o, lse, BH, N, scale, stream)
-                      : launch_fwd_t<128, false>(q, k, v, o, lse, BH, N, scale, stream);
+        return causal ? launch_fwd_w64<true>(q, k, v, o, lse, BH, N, scale, stream)
+                      : launch_fwd_w64<false>(q, k, v, o, lse, BH, N, scale, stream);
     return causal ? launch_fwd_t<64, true>(q, k, v, o, lse, BH, N, scale, stream)
                   : launch_fwd_t<64, false>(q, k, v, o, lse, BH, N, scale, stream);
 }

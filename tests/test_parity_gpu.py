@@ -75,7 +75,17 @@ def _compare(out, ref, cfg, heads, floor=None):
 SMALL = [
     ("tiny_causal", "gaussian"), ("tiny_causal", "wide_logits"), ("tiny_causal", "late_spike"),
     ("noncausal", "gaussian"), ("noncausal", "wide_logits"), ("noncausal", "late_spike"),
+    # d = 128 with several 256-row query tiles and 64-key tiles plus a ragged
+    # end: the adversarial regimes move the running row max by far more than
+    # the forward's lazy-rescale threshold
+    ("adv_c128", "wide_logits"), ("adv_c128", "late_spike"),
+    ("adv_n128", "wide_logits"), ("adv_n128", "late_spike"),
 ]
+
+ADV = {
+    "adv_c128": DenseConfig("adv_c128", 1, 2, 600, 128, True, seed=11),
+    "adv_n128": DenseConfig("adv_n128", 1, 2, 520, 128, False, seed=12),
+}
 
 RAGGED = [
     DenseConfig("ragged_c128", 1, 3, 333, 128, True, seed=1),
@@ -95,7 +105,7 @@ RAGGED = [
 
 @pytest.mark.parametrize("name,regime", SMALL)
 def test_small_end_to_end(lib, name, regime):
-    cfg = DENSE_CONFIGS[name]
+    cfg = DENSE_CONFIGS.get(name) or ADV[name]
     say(f"[parity] {name} {regime} B{cfg.B} H{cfg.H} N{cfg.N} d{cfg.d} causal={cfg.causal}")
     inp = make_dense_inputs(cfg, regime)
     out = _gpu_path(lib, inp, cfg)
