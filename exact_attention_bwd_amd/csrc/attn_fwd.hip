@@ -313,6 +313,14 @@ __device__ __forceinline__ void mfma_mask(f32x16& c, const bf16x8& a0, const bf1
         : "v"(a0), "v"(a1), "v"(b0), "v"(b1));
 }
 
+// max(a, b, c) without the canonicalising v_max the compiler puts in front of
+// every fmaxf operand that it cannot prove canonical (the MFMA results)
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 // x of lane l combined with x of lane l ^ 32: v_permlane32_swap exchanges the
 // upper half of one register with the lower half of another, so both halves
 // of a copy end up holding the other lane's value (no LDS involved)
@@ -339,6 +347,10 @@ __device__ __forceinline__ float pair_sum(float x) {
         : "+v"(x), "=&v"(y));
     return x;
 }
+
+// first element of tile t + 1 whose exponential the PV phase's slot m (8 .. 31)
+// evaluates: 32 elements over 24 slots
+constexpr int pv_e(int m) { return m <= 8 ? 0 : ((m - 8) * 4) / 3; }
 
 template <bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(WNW * 64, WNW * 64), amdgpu_waves_per_eu(1, 1)))
@@ -416,6 +428,9 @@ void fwd_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 
     // row reads of K: chunk 2 ks + g of row 32 kb + l32 at (aK ^ 32 ks) + 8 KiB kb
     const uint32_t aK = lds_addr(smem) + (uint32_t)(roff<HD>(l32, g) * 2);
+    uint32_t aKs[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) aKs[ks] = aK ^ (uint32_t)(ks * 32);
     // transposing reads of V (A operand V^T): rows 4 g + s4 (+ 16 k4, + 8),
     // columns 16 hh + 4 (t16 & 3) (+ 32 db); bases of the current V slot
     const int otr = roff4<HD>(g * 4 + s4, hh * 16 + 4 * (t16 & 3));
@@ -452,7 +467,7 @@ void fwd_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     auto issue = [&](auto jI, auto ksI) __attribute__((always_inline)) {
         constexpr int j = decltype(jI)::value, KS = decltype(ksI)::value;
         if constexpr (j < 16) {
-            lds_ld_a<S::off_k + KS * S::TILE + (j >> 3) * 8192>(kop[j], vxor<(j & 7) * 32>(aK));
+            lds_ld_a<S::off_k + KS * S::TILE + (j >> 3) * 8192>(kop[j], aKs[j & 7]);
         } else {
             constexpr int v = j - 16;
             tr_read2o<(v >> 2) * 4096>(vop[v][0], vop[v][1], trv[v & 3][0], trv[v & 3][1]);
@@ -464,24 +479,43 @@ void fwd_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     // operand (row block qb, key step k4), k4 = u / 8, qb = (u / 4) % 2, dword
     // i = u % 4, i.e. accumulator entry r = 8 (k4 % 2) + 2 i + e % 2 of key
     // block k4 / 2.  Elements 0 .. 31 are key block 0, 32 .. 63 key block 1.
-    auto elem = [&](f32x16(&s)[2][2], auto eI, auto pinI) __attribute__((always_inline)) {
+    auto elem = [&](f32x16(&s)[2][2], auto eI) __attribute__((always_inline)) {
         constexpr int e = decltype(eI)::value;
-        constexpr bool PIN = decltype(pinI)::value;
         constexpr int u = e >> 1, jj = e & 1, k4 = u >> 3, qb = (u >> 2) & 1, i = u & 3;
         constexpr int kb = k4 >> 1, r = 8 * (k4 & 1) + 2 * i + jj;
         const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][r], sl2, -mrow[qb]));
         lrow[qb] += p;
-        // pinned in the loop: the compiler would otherwise sink the sums and
-        // packs towards their uses in the next iteration, past the rescale
-        // branch
-        if constexpr (PIN) asm volatile("" : "+v"(lrow[qb]));
         if constexpr (jj == 0) {
             phold = p;
         } else {
             typedef float f32x2 __attribute__((ext_vector_type(2)));
             typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
             pk[qb][k4][i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{phold, p}, bf16x2));
-            if constexpr (PIN) asm volatile("" : "+v"(pk[qb][k4]));
+        }
+    };
+    // The same in two halves for the pipelined loop, issued one MFMA slot
+    // apart so that no instruction waits for the exponential's result:
+    // elem_exp leaves p in pbuf[e % 4], elem_sum adds it to l and packs pairs.
+    float pbuf[4];
+    auto elem_exp = [&](f32x16(&s)[2][2], auto eI) __attribute__((always_inline)) {
+        constexpr int e = decltype(eI)::value;
+        constexpr int u = e >> 1, k4 = u >> 3, qb = (u >> 2) & 1, i = u & 3;
+        constexpr int kb = k4 >> 1, r = 8 * (k4 & 1) + 2 * i + (e & 1);
+        pbuf[e & 3] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][r], sl2, -mrow[qb]));
+    };
+    auto elem_sum = [&](auto eI) __attribute__((always_inline)) {
+        constexpr int e = decltype(eI)::value;
+        constexpr int u = e >> 1, k4 = u >> 3, qb = (u >> 2) & 1, i = u & 3;
+        lrow[qb] += pbuf[e & 3];
+        // pinned here: the compiler would otherwise sink the sums and packs
+        // towards their uses in the next iteration, past the rescale branch
+        asm volatile("" : "+v"(lrow[qb]));
+        if constexpr (e & 1) {
+            typedef float f32x2 __attribute__((ext_vector_type(2)));
+            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+            pk[qb][k4][i] = __builtin_bit_cast(
+                uint32_t, __builtin_convertvector(f32x2{pbuf[(e - 1) & 3], pbuf[e & 3]}, bf16x2));
+            asm volatile("" : "+v"(pk[qb][k4]));
         }
     };
     // Masking on the matrix core.  In block (qb, kb) of a tile, S^T entry
@@ -512,7 +546,7 @@ void fwd_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     };
     auto max8 = [&](float m, const f32x16& s, int h) __attribute__((always_inline)) {
 #pragma unroll
-        for (int r = 0; r < 8; ++r) m = __builtin_fmaxf(m, s[8 * h + r]);
+        for (int r = 0; r < 8; r += 2) m = max3f(m, s[8 * h + r], s[8 * h + r + 1]);
         return m;
     };
     // new offset of row block qb from its tile max pmax (this lane's keys)
@@ -559,7 +593,7 @@ void fwd_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         pmax[qb] = max8(max8(max8(max8(-__builtin_inff(), sa[qb][0], 0), sa[qb][0], 1), sa[qb][1], 0), sa[qb][1], 1);
     combine(0);
     combine(1);
-    static_for<0, 32>([&](auto eI) __attribute__((always_inline)) { elem(sa, eI, std::false_type{}); });
+    static_for<0, 32>([&](auto eI) __attribute__((always_inline)) { elem(sa, eI); });
 
     // ---- main loop.  Slot rules (B_t = the barrier of iteration t):
     //  * iteration t reads K_{t+1} (S phase; its first D operands are issued
@@ -586,7 +620,8 @@ void fwd_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
             }
             if constexpr (ks == 0) mfma_q0(sn[qb][kb], kop[n], qa[qb][ks]);
             else mfma_q(sn[qb][kb], kop[n], qa[qb][ks]);
-            elem(sc, std::integral_constant<int, 32 + m>{}, std::true_type{});
+            elem_exp(sc, std::integral_constant<int, 32 + m>{});
+            if constexpr (m > 0) elem_sum(std::integral_constant<int, 32 + m - 1>{});
             // mask and row max of S(t+1), key block 0 (its last products: slots 14, 15)
             if constexpr (m == 16) {
                 mask(sn, I0{}, I0{}, t + 1);
@@ -596,8 +631,7 @@ void fwd_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
             if constexpr (m >= 17 && m < 25) {
                 constexpr int b = (m - 17) >> 2, h = (m - 17) & 3;
                 if constexpr (h == 0) pmax[b] = -__builtin_inff();
-                pmax[b] = __builtin_fmaxf(pmax[b], __builtin_fmaxf(__builtin_fmaxf(sn[b][0][4 * h], sn[b][0][4 * h + 1]),
-                                                                   __builtin_fmaxf(sn[b][0][4 * h + 2], sn[b][0][4 * h + 3])));
+                pmax[b] = max3f(max3f(pmax[b], sn[b][0][4 * h], sn[b][0][4 * h + 1]), sn[b][0][4 * h + 2], sn[b][0][4 * h + 3]);
             }
             __builtin_amdgcn_sched_barrier(0);
         });
@@ -624,12 +658,16 @@ void fwd_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
             if constexpr (m < 4) pmax[m >> 1] = max8(pmax[m >> 1], sn[m >> 1][1], m & 1);
             if constexpr (m == 4) combine(0);
             if constexpr (m == 5) combine(1);
+            if constexpr (m == 0) elem_sum(std::integral_constant<int, 63>{});   // tile t's last
             if constexpr (m >= 8) {
-                constexpr int e0 = ((m - 8) * 4) / 3, e1 = ((m - 7) * 4) / 3;
-                static_for<e0, e1>([&](auto eI) __attribute__((always_inline)) { elem(sn, eI, std::true_type{}); });
+                static_for<pv_e(m), pv_e(m + 1)>([&](auto eI) __attribute__((always_inline)) { elem_exp(sn, eI); });
+            }
+            if constexpr (m >= 9) {
+                static_for<pv_e(m - 1), pv_e(m)>([&](auto eI) __attribute__((always_inline)) { elem_sum(eI); });
             }
             __builtin_amdgcn_sched_barrier(0);
         });
+        static_for<pv_e(31), pv_e(32)>([&](auto eI) __attribute__((always_inline)) { elem_sum(eI); });
         // lazy rescale of O^T, after the last product that used the old offset
         if (__builtin_expect(pend[0] || pend[1], 0)) {
             asm volatile("s_nop 15\n\ts_nop 15"
