@@ -28,6 +28,10 @@
 #include "launch.hpp"
 #include "tiles.hpp"
 
+#ifndef FWD_RB
+#define FWD_RB 1
+#endif
+
 namespace attn {
 namespace fwd {
 
@@ -274,7 +278,6 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 //    with the count FwdSched derives from the issue order.
 // ----------------------------------------------------------------------------
 constexpr int WBM = 256;                 // query rows per workgroup
-constexpr int WNW = 4;                   // wave64s per workgroup
 
 struct WSmem {
     static constexpr int TILE = BN * 128 * 2;        // one K or V tile: 16 KiB
@@ -348,16 +351,40 @@ __device__ __forceinline__ float pair_sum(float x) {
     return x;
 }
 
-// first element of tile t + 1 whose exponential the PV phase's slot m (8 .. 31)
-// evaluates: 32 elements over 24 slots
-constexpr int pv_e(int m) { return m <= 8 ? 0 : ((m - 8) * 4) / 3; }
+// first element of tile t + 1 whose exponential slot m of the PV phase
+// evaluates (RB 32-row blocks per wave: slots 4 RB .. 16 RB - 1 take the
+// 16 RB elements of key block 0)
+constexpr int pv_e(int m, int RB) { return m <= 4 * RB ? 0 : ((m - 4 * RB) * 4) / 3; }
 
-template <bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(WNW * 64, WNW * 64), amdgpu_waves_per_eu(1, 1)))
+// 16 wait states tied to the accumulators a VALU instruction reads next
+template <int RB>
+__device__ __forceinline__ void settle(f32x16 (&s)[RB][2], int kb) {
+    if constexpr (RB == 2) asm volatile("s_nop 15" : "+v"(s[0][kb]), "+v"(s[1][kb]));
+    else asm volatile("s_nop 15" : "+v"(s[0][kb]));
+}
+
+template <int RB>
+__device__ __forceinline__ void settle_o(f32x16 (&o)[RB][4]) {
+    if constexpr (RB == 2)
+        asm volatile("s_nop 15\n\ts_nop 15"
+                     : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[0][2]), "+a"(o[0][3]),
+                       "+a"(o[1][0]), "+a"(o[1][1]), "+a"(o[1][2]), "+a"(o[1][3]));
+    else
+        asm volatile("s_nop 15\n\ts_nop 15" : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[0][2]), "+a"(o[0][3]));
+}
+
+// RB = 2: 4 waves (one per SIMD), 64 rows each; RB = 1: 8 waves (two per
+// SIMD), 32 rows each.  Both cover a 256-row query tile.
+template <bool CAUSAL, int RB>
+__global__ __attribute__((amdgpu_flat_work_group_size(512 / RB, 512 / RB), amdgpu_waves_per_eu(3 - RB, 3 - RB)))
 void fwd_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                     const __bf16* __restrict__ V, __bf16* __restrict__ O, float* __restrict__ Lse,
                     int BH, int N, float scale) {
     constexpr int HD = 128;
+    constexpr int NW = 8 / RB;                   // waves per workgroup
+    constexpr int EPT = 32 * RB;                 // softmax elements per lane per key tile
+    constexpr int H = EPT / 2;                   // of which key block 0
+    constexpr int NS = 16 * RB;                  // MFMA slots per phase
     using SC = FwdSched;
     using S = WSmem;
     using I0 = std::integral_constant<int, 0>;
@@ -396,17 +423,17 @@ void fwd_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     }
     const int q0 = qt * WBM;
     const int qrows = min(N - q0, WBM);
-    const int qw = 64 * w;                       // this wave's first row in the tile
+    const int qw = 32 * RB * w;                  // this wave's first row in the tile
     const size_t head = (size_t)bh * N * HD;
     const __bf16* Kh = K + head;
     const __bf16* Vh = V + head;
     const int T = CAUSAL ? (q0 + qrows - 1) / BN + 1 : (N + BN - 1) / BN;   // key tiles
 
     // Q rows of this lane as B operands of S^T: Q[qw + 32 qb + l32][16 ks + 8 g ..]
-    bf16x8 qa[2][8];
+    bf16x8 qa[RB][8];
     {
         const __amdgpu_buffer_rsrc_t qr = make_rsrc(Q + head + (size_t)q0 * HD, qrows * HD * 2);
-        static_for<0, 2>([&](auto qbI) __attribute__((always_inline)) {
+        static_for<0, RB>([&](auto qbI) __attribute__((always_inline)) {
             constexpr int qb = decltype(qbI)::value;
             static_for<0, 8>([&](auto ksI) __attribute__((always_inline)) {
                 constexpr int ks = decltype(ksI)::value;
@@ -417,13 +444,13 @@ void fwd_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         });
     }
 
-    int voff[BN * (HD / 8) / 64 / WNW];
-    stage_offsets<HD, BN, WNW>(voff, w, lane);
+    int voff[BN * (HD / 8) / 64 / NW];
+    stage_offsets<HD, BN, NW>(voff, w, lane);
     // tiles at or past T (padding of the last iteration) are filled with zeros
     auto dma = [&](const __bf16* base, int tile, int lds_off) __attribute__((always_inline)) {
         const int n0 = tile * BN;
         const int bytes = tile < T ? min(N - n0, BN) * HD * 2 : 0;
-        stage_rows_b<HD, BN, WNW>(make_rsrc(base + (size_t)min(n0, N - 1) * HD, bytes), voff, smem + lds_off, w);
+        stage_rows_b<HD, BN, NW>(make_rsrc(base + (size_t)min(n0, N - 1) * HD, bytes), voff, smem + lds_off, w);
     };
 
     // row reads of K: chunk 2 ks + g of row 32 kb + l32 at (aK ^ 32 ks) + 8 KiB kb
@@ -440,27 +467,25 @@ void fwd_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         trv[db][0] = lds_addr(smem + S::off_v) + (uint32_t)((otr ^ (db << 5)) * 2);
         trv[db][1] = lds_addr(smem + S::off_v) + (uint32_t)((((otr + 8 * HD) ^ (db << 5)) ^ 16) * 2);
     }
-    // A operand of the mask product: ones where key l32 >= k (k = 16 h + 8 g + e)
-    bf16x8 tri[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) tri[h][e] = l32 >= 16 * h + 8 * g + e ? (__bf16)1.f : (__bf16)0.f;
 
-    f32x16 sa[2][2], sb[2][2];                   // S^T of tiles t (t even: sa) and t + 1
-    f32x16 o[2][4];                              // O^T, rows = head dim, in AGPRs
+    f32x16 sa[RB][2], sb[RB][2];                 // S^T of tiles t (t even: sa) and t + 1
+    f32x16 o[RB][4];                             // O^T, rows = head dim, in AGPRs
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int qb = 0; qb < RB; ++qb)
 #pragma unroll
         for (int db = 0; db < 4; ++db) o[qb][db] = zero16();
-    u32x4 pk[2][4];                              // P^T operands (bf16 pairs)
+    u32x4 pk[RB][4];                             // P^T operands (bf16 pairs)
     bf16x8 kop[16];
     u32x2 vop[16][2];
-    float mrow[2] = {-__builtin_inff(), -__builtin_inff()};   // exponent offset (log2 units)
-    float lrow[2] = {0.f, 0.f};                  // this lane's share of the normaliser
-    float oa[2] = {1.f, 1.f};                    // pending O rescale factor
-    float pmax[2];
-    bool pend[2] = {false, false};
+    float mrow[RB], lrow[RB], oa[RB], pmax[RB];
+    bool pend[RB];
+#pragma unroll
+    for (int qb = 0; qb < RB; ++qb) {
+        mrow[qb] = -__builtin_inff();            // exponent offset (log2 units)
+        lrow[qb] = 0.f;                          // this lane's share of the normaliser
+        oa[qb] = 1.f;                            // pending O rescale factor
+        pend[qb] = false;
+    }
     const float sl2 = scale * kLog2e;
 
     // operand j of an iteration whose K rows are in K slot KS
@@ -473,73 +498,83 @@ void fwd_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
             tr_read2o<(v >> 2) * 4096>(vop[v][0], vop[v][1], trv[v & 3][0], trv[v & 3][1]);
         }
     };
+    // element e (0 .. EPT - 1) of a tile's S^T: p = 2^(S scale log2 e - m),
+    // added to l and packed in pairs into the P^T operands.  e -> pair u = e / 2
+    // of operand (row block qb, key step k4), k4 = u / (4 RB), qb = (u / 4) % RB,
+    // dword i = u % 4, i.e. accumulator entry r = 8 (k4 % 2) + 2 i + e % 2 of
+    // key block k4 / 2.  The first half of the elements is key block 0.
+    struct Ix {
+        int qb, kb, k4, i, r;
+    };
+    constexpr auto ix = [](int e) constexpr {
+        const int u = e >> 1, k4 = u / (4 * RB);
+        return Ix{(u >> 2) % RB, k4 >> 1, k4, u & 3, 8 * (k4 & 1) + 2 * (u & 3) + (e & 1)};
+    };
     float phold = 0.f;                           // first element of a pair
-    // element e (0 .. 63) of a tile's S^T: p = 2^(S scale log2 e - m), added to
-    // l and packed in pairs into the P^T operands.  e -> pair u = e / 2 of
-    // operand (row block qb, key step k4), k4 = u / 8, qb = (u / 4) % 2, dword
-    // i = u % 4, i.e. accumulator entry r = 8 (k4 % 2) + 2 i + e % 2 of key
-    // block k4 / 2.  Elements 0 .. 31 are key block 0, 32 .. 63 key block 1.
-    auto elem = [&](f32x16(&s)[2][2], auto eI) __attribute__((always_inline)) {
+    auto elem = [&](f32x16(&s)[RB][2], auto eI) __attribute__((always_inline)) {
         constexpr int e = decltype(eI)::value;
-        constexpr int u = e >> 1, jj = e & 1, k4 = u >> 3, qb = (u >> 2) & 1, i = u & 3;
-        constexpr int kb = k4 >> 1, r = 8 * (k4 & 1) + 2 * i + jj;
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][r], sl2, -mrow[qb]));
-        lrow[qb] += p;
-        if constexpr (jj == 0) {
+        constexpr Ix x = ix(e);
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[x.qb][x.kb][x.r], sl2, -mrow[x.qb]));
+        lrow[x.qb] += p;
+        if constexpr ((e & 1) == 0) {
             phold = p;
         } else {
             typedef float f32x2 __attribute__((ext_vector_type(2)));
             typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-            pk[qb][k4][i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{phold, p}, bf16x2));
+            pk[x.qb][x.k4][x.i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{phold, p}, bf16x2));
         }
     };
     // The same in two halves for the pipelined loop, issued one MFMA slot
     // apart so that no instruction waits for the exponential's result:
     // elem_exp leaves p in pbuf[e % 4], elem_sum adds it to l and packs pairs.
     float pbuf[4];
-    auto elem_exp = [&](f32x16(&s)[2][2], auto eI) __attribute__((always_inline)) {
+    auto elem_exp = [&](f32x16(&s)[RB][2], auto eI) __attribute__((always_inline)) {
         constexpr int e = decltype(eI)::value;
-        constexpr int u = e >> 1, k4 = u >> 3, qb = (u >> 2) & 1, i = u & 3;
-        constexpr int kb = k4 >> 1, r = 8 * (k4 & 1) + 2 * i + (e & 1);
-        pbuf[e & 3] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][r], sl2, -mrow[qb]));
+        constexpr Ix x = ix(e);
+        pbuf[e & 3] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[x.qb][x.kb][x.r], sl2, -mrow[x.qb]));
     };
     auto elem_sum = [&](auto eI) __attribute__((always_inline)) {
         constexpr int e = decltype(eI)::value;
-        constexpr int u = e >> 1, k4 = u >> 3, qb = (u >> 2) & 1, i = u & 3;
-        lrow[qb] += pbuf[e & 3];
+        constexpr Ix x = ix(e);
+        lrow[x.qb] += pbuf[e & 3];
         // pinned here: the compiler would otherwise sink the sums and packs
         // towards their uses in the next iteration, past the rescale branch
-        asm volatile("" : "+v"(lrow[qb]));
+        asm volatile("" : "+v"(lrow[x.qb]));
         if constexpr (e & 1) {
             typedef float f32x2 __attribute__((ext_vector_type(2)));
             typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-            pk[qb][k4][i] = __builtin_bit_cast(
+            pk[x.qb][x.k4][x.i] = __builtin_bit_cast(
                 uint32_t, __builtin_convertvector(f32x2{pbuf[(e - 1) & 3], pbuf[e & 3]}, bf16x2));
-            asm volatile("" : "+v"(pk[qb][k4]));
+            asm volatile("" : "+v"(pk[x.qb][x.k4]));
         }
     };
     // Masking on the matrix core.  In block (qb, kb) of a tile, S^T entry
     // (key k, row q) must become -inf when k > thr(q) = min(row, N - 1) - key
     // offset.  With c(q) = clamp(thr(q) + 1, 0, 32), the product of the
-    // constant 32 x 32 matrix [k >= k'] (tri) and the matrix B[k'][q] = -2^120
-    // for k' = c(q), else 0, adds -2^120 exactly to the masked entries and 0 to
+    // constant 32 x 32 matrix [k >= k'] and the matrix B[k'][q] = -2^120 for
+    // k' = c(q), else 0, adds -2^120 exactly to the masked entries and 0 to
     // the others; -2^120 scale log2 e underflows 2^x to 0 and never wins a
     // row max.  Only blocks that reach past a row or past N take it (a
     // wave-uniform branch around two MFMAs that update the block in place).
-    auto mask = [&](f32x16(&s)[2][2], auto qbI, auto kbI, int tile) __attribute__((always_inline)) {
+    // ALWAYS: no branch (the product adds zeros where nothing is masked);
+    // used once, where a branch would only make the compiler copy the block
+    auto mask = [&](f32x16(&s)[RB][2], auto qbI, auto kbI, int tile, auto alwaysI) __attribute__((always_inline)) {
         constexpr int qb = decltype(qbI)::value, kb = decltype(kbI)::value;
         const int kofs = tile * BN + 32 * kb;
         const int qrow0 = q0 + qw + 32 * qb;
-        if ((CAUSAL && kofs + 31 > qrow0) || kofs + 31 > N - 1) {
+        if (decltype(alwaysI)::value || (CAUSAL && kofs + 31 > qrow0) || kofs + 31 > N - 1) {
             const int lim = CAUSAL ? min(qrow0 + l32, N - 1) : N - 1;
             const int c = min(max(lim - kofs + 1, 0), 32);
             u32x4 bm[2];
+            bf16x8 tri[2];                       // A operand: ones where key l32 >= k, k = 16 h + 8 g + e
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int idx = c - 16 * h - 8 * g;    // element of this lane's operand that is hit
 #pragma unroll
                 for (int d = 0; d < 4; ++d)
                     bm[h][d] = (idx >> 1) == d ? ((idx & 1) ? 0xFB800000u : 0x0000FB80u) : 0u;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) tri[h][e] = l32 >= 16 * h + 8 * g + e ? (__bf16)1.f : (__bf16)0.f;
             }
             mfma_mask(s[qb][kb], tri[0], tri[1], __builtin_bit_cast(bf16x8, bm[0]), __builtin_bit_cast(bf16x8, bm[1]));
         }
@@ -567,8 +602,8 @@ void fwd_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     dma(Vh, 0, S::off_v);
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     static_for<0, SC::D>([&](auto jI) __attribute__((always_inline)) { issue(jI, I0{}); });
-    static_for<0, 32>([&](auto mI) __attribute__((always_inline)) {
-        constexpr int m = decltype(mI)::value, n = m >> 1, qb = m & 1, kb = n >> 3, ks = n & 7;
+    static_for<0, NS>([&](auto mI) __attribute__((always_inline)) {
+        constexpr int m = decltype(mI)::value, n = m / RB, qb = m % RB, kb = n >> 3, ks = n & 7;
         if constexpr (qb == 0) {
             if constexpr (SC::issues(SC::PRO, n)) issue(std::integral_constant<int, n + SC::D>{}, I0{});
             lgkm_wait_a<SC::wait(SC::PRO, n)>(kop[n]);
@@ -582,18 +617,18 @@ void fwd_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     dma(Kh, 2, S::off_k);
     dma(Vh, 1, S::off_v + S::TILE);
     static_for<0, SC::D>([&](auto jI) __attribute__((always_inline)) { issue(jI, I1{}); });   // K_1, iteration 0
-    static_for<0, 2>([&](auto qbI) __attribute__((always_inline)) {
-        mask(sa, qbI, I0{}, 0);
-        mask(sa, qbI, I1{}, 0);
+    static_for<0, RB>([&](auto qbI) __attribute__((always_inline)) {
+        mask(sa, qbI, I0{}, 0, std::true_type{});
+        mask(sa, qbI, I1{}, 0, std::true_type{});
     });
-    mfma_v_settle2(sa[0][0], sa[0][1]);
-    mfma_v_settle2(sa[1][0], sa[1][1]);
+    settle<RB>(sa, 0);
+    settle<RB>(sa, 1);
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int qb = 0; qb < RB; ++qb) {
         pmax[qb] = max8(max8(max8(max8(-__builtin_inff(), sa[qb][0], 0), sa[qb][0], 1), sa[qb][1], 0), sa[qb][1], 1);
-    combine(0);
-    combine(1);
-    static_for<0, 32>([&](auto eI) __attribute__((always_inline)) { elem(sa, eI); });
+        combine(qb);
+    }
+    static_for<0, H>([&](auto eI) __attribute__((always_inline)) { elem(sa, eI); });
 
     // ---- main loop.  Slot rules (B_t = the barrier of iteration t):
     //  * iteration t reads K_{t+1} (S phase; its first D operands are issued
@@ -608,11 +643,11 @@ void fwd_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     auto iter = [&](auto pI, int t) __attribute__((always_inline)) {
         constexpr int p = decltype(pI)::value;
         constexpr int KS = p ^ 1;               // K slot of tile t + 1
-        f32x16(&sc)[2][2] = p ? sb : sa;         // tile t
-        f32x16(&sn)[2][2] = p ? sa : sb;         // tile t + 1
+        f32x16(&sc)[RB][2] = p ? sb : sa;        // tile t
+        f32x16(&sn)[RB][2] = p ? sa : sb;        // tile t + 1
         // ---- S phase: S(t+1); exponentials of tile t, key block 1
-        static_for<0, 32>([&](auto mI) __attribute__((always_inline)) {
-            constexpr int m = decltype(mI)::value, n = m >> 1, qb = m & 1, kb = n >> 3, ks = n & 7;
+        static_for<0, NS>([&](auto mI) __attribute__((always_inline)) {
+            constexpr int m = decltype(mI)::value, n = m / RB, qb = m % RB, kb = n >> 3, ks = n & 7;
             if constexpr (qb == 0) {
                 if constexpr (SC::issues(SC::ITER, n))
                     issue(std::integral_constant<int, n + SC::D>{}, std::integral_constant<int, KS>{});
@@ -620,24 +655,24 @@ void fwd_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
             }
             if constexpr (ks == 0) mfma_q0(sn[qb][kb], kop[n], qa[qb][ks]);
             else mfma_q(sn[qb][kb], kop[n], qa[qb][ks]);
-            elem_exp(sc, std::integral_constant<int, 32 + m>{});
-            if constexpr (m > 0) elem_sum(std::integral_constant<int, 32 + m - 1>{});
-            // mask and row max of S(t+1), key block 0 (its last products: slots 14, 15)
-            if constexpr (m == 16) {
-                mask(sn, I0{}, I0{}, t + 1);
-                mask(sn, I1{}, I0{}, t + 1);
-                mfma_v_settle2(sn[0][0], sn[1][0]);
+            elem_exp(sc, std::integral_constant<int, H + m>{});
+            if constexpr (m > 0) elem_sum(std::integral_constant<int, H + m - 1>{});
+            // mask and row max of S(t+1), key block 0 (its last products: the
+            // slots before 8 RB)
+            if constexpr (m == 8 * RB) {
+                static_for<0, RB>([&](auto qbI) __attribute__((always_inline)) { mask(sn, qbI, I0{}, t + 1, std::false_type{}); });
+                settle<RB>(sn, 0);
             }
-            if constexpr (m >= 17 && m < 25) {
-                constexpr int b = (m - 17) >> 2, h = (m - 17) & 3;
+            if constexpr (m > 8 * RB && m <= 12 * RB) {
+                constexpr int b = (m - 8 * RB - 1) >> 2, h = (m - 8 * RB - 1) & 3;
                 if constexpr (h == 0) pmax[b] = -__builtin_inff();
                 pmax[b] = max3f(max3f(pmax[b], sn[b][0][4 * h], sn[b][0][4 * h + 1]), sn[b][0][4 * h + 2], sn[b][0][4 * h + 3]);
             }
             __builtin_amdgcn_sched_barrier(0);
         });
         // ---- PV phase: O^T += V_t^T P_t^T; row max and key block 0 of tile t + 1
-        static_for<0, 32>([&](auto mI) __attribute__((always_inline)) {
-            constexpr int m = decltype(mI)::value, v = m >> 1, qb = m & 1, db = v & 3, k4 = v >> 2;
+        static_for<0, NS>([&](auto mI) __attribute__((always_inline)) {
+            constexpr int m = decltype(mI)::value, v = m / RB, qb = m % RB, db = v & 3, k4 = v >> 2;
             constexpr int n = 16 + v;
             if constexpr (qb == 0) {
                 if constexpr (n == SC::BARRIER_N) {
@@ -651,29 +686,28 @@ void fwd_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
             }
             mfma_o(o[qb][db], cat_u(vop[v][0], vop[v][1]), __builtin_bit_cast(bf16x8, pk[qb][k4]));
             if constexpr (m == 0) {
-                mask(sn, I0{}, I1{}, t + 1);
-                mask(sn, I1{}, I1{}, t + 1);
-                mfma_v_settle2(sn[0][1], sn[1][1]);      // last S(t+1) products: S slots 30, 31
+                static_for<0, RB>([&](auto qbI) __attribute__((always_inline)) { mask(sn, qbI, I1{}, t + 1, std::false_type{}); });
+                settle<RB>(sn, 1);                // last S(t+1) products: the last S slots
+                elem_sum(std::integral_constant<int, EPT - 1>{});   // tile t's last
             }
-            if constexpr (m < 4) pmax[m >> 1] = max8(pmax[m >> 1], sn[m >> 1][1], m & 1);
-            if constexpr (m == 4) combine(0);
-            if constexpr (m == 5) combine(1);
-            if constexpr (m == 0) elem_sum(std::integral_constant<int, 63>{});   // tile t's last
-            if constexpr (m >= 8) {
-                static_for<pv_e(m), pv_e(m + 1)>([&](auto eI) __attribute__((always_inline)) { elem_exp(sn, eI); });
+            if constexpr (m < 2 * RB) pmax[m >> 1] = max8(pmax[m >> 1], sn[m >> 1][1], m & 1);
+            if constexpr (m >= 2 * RB && m < 3 * RB) combine(m - 2 * RB);
+            if constexpr (m >= 4 * RB) {
+                static_for<pv_e(m, RB), pv_e(m + 1, RB)>([&](auto eI) __attribute__((always_inline)) { elem_exp(sn, eI); });
             }
-            if constexpr (m >= 9) {
-                static_for<pv_e(m - 1), pv_e(m)>([&](auto eI) __attribute__((always_inline)) { elem_sum(eI); });
+            if constexpr (m > 4 * RB) {
+                static_for<pv_e(m - 1, RB), pv_e(m, RB)>([&](auto eI) __attribute__((always_inline)) { elem_sum(eI); });
             }
             __builtin_amdgcn_sched_barrier(0);
         });
-        static_for<pv_e(31), pv_e(32)>([&](auto eI) __attribute__((always_inline)) { elem_sum(eI); });
+        static_for<pv_e(NS - 1, RB), pv_e(NS, RB)>([&](auto eI) __attribute__((always_inline)) { elem_sum(eI); });
         // lazy rescale of O^T, after the last product that used the old offset
-        if (__builtin_expect(pend[0] || pend[1], 0)) {
-            asm volatile("s_nop 15\n\ts_nop 15"
-                         : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[0][2]), "+a"(o[0][3]),
-                           "+a"(o[1][0]), "+a"(o[1][1]), "+a"(o[1][2]), "+a"(o[1][3]));
-            static_for<0, 2>([&](auto qbI) __attribute__((always_inline)) {
+        bool any = false;
+#pragma unroll
+        for (int qb = 0; qb < RB; ++qb) any = any || pend[qb];
+        if (__builtin_expect(any, 0)) {
+            settle_o<RB>(o);
+            static_for<0, RB>([&](auto qbI) __attribute__((always_inline)) {
                 constexpr int qb = decltype(qbI)::value;
                 if (pend[qb]) {
                     static_for<0, 4>([&](auto dbI) __attribute__((always_inline)) {
@@ -701,11 +735,9 @@ void fwd_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // copies issued for tiles past the end
 
     // ---- O = O^T / l, L = (m + log2 l) ln 2
-    asm volatile("s_nop 15\n\ts_nop 15"
-                 : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[0][2]), "+a"(o[0][3]),
-                   "+a"(o[1][0]), "+a"(o[1][1]), "+a"(o[1][2]), "+a"(o[1][3]));
+    settle_o<RB>(o);
     const __amdgpu_buffer_rsrc_t orc = make_rsrc(O + head + (size_t)q0 * HD, qrows * HD * 2);
-    static_for<0, 2>([&](auto qbI) __attribute__((always_inline)) {
+    static_for<0, RB>([&](auto qbI) __attribute__((always_inline)) {
         constexpr int qb = decltype(qbI)::value;
         const float lt = pair_sum(lrow[qb]);
         const float inv = 1.f / lt;
@@ -743,11 +775,12 @@ template <bool CAUSAL>
 static hipError_t launch_fwd_w64(const void* q, const void* k, const void* v, void* o, float* lse,
                                  int BH, int N, float scale, hipStream_t stream) {
     using S = fwd::WSmem;
-    auto kern = fwd::fwd_w64_kernel<CAUSAL>;
+    constexpr int RB = FWD_RB;
+    auto kern = fwd::fwd_w64_kernel<CAUSAL, RB>;
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, S::bytes);
     if (e != hipSuccess) return e;
     const int tq = (N + fwd::WBM - 1) / fwd::WBM;
-    hipLaunchKernelGGL(kern, dim3(BH * tq), dim3(fwd::WNW * 64), S::bytes, stream, (const __bf16*)q,
+    hipLaunchKernelGGL(kern, dim3(BH * tq), dim3(512 / RB), S::bytes, stream, (const __bf16*)q,
                        (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, BH, N, scale);
     return hipGetLastError();
 }

@@ -20,7 +20,7 @@ namespace attn {
 namespace fwd {
 
 struct FwdSched {
-    static constexpr int D = 4;                  // operands in flight
+    static constexpr int D = 3;                  // operands in flight
     static constexpr int NOPS = 32;              // operands per iteration
     static constexpr int NK = 16;                // of which K rows
     // stream modes

@@ -28,8 +28,8 @@ KERNELS = (
     ("attn_bwd.hip", "_ZN4attn3bwd13bwd_dq_kernelILi128ELb0E"),
     ("attn_bwd.hip", "_ZN4attn3bwd13bwd_dq_kernelILi64ELb1E"),
     ("attn_bwd.hip", "_ZN4attn3bwd13bwd_dq_kernelILi64ELb0E"),
-    ("attn_fwd.hip", "_ZN4attn3fwd14fwd_w64_kernelILb1E"),
-    ("attn_fwd.hip", "_ZN4attn3fwd14fwd_w64_kernelILb0E"),
+    ("attn_fwd.hip", "_ZN4attn3fwd14fwd_w64_kernelILb1ELi1E"),
+    ("attn_fwd.hip", "_ZN4attn3fwd14fwd_w64_kernelILb0ELi1E"),
 )
 
 
