@@ -164,6 +164,20 @@ def make_dense_inputs(cfg: DenseConfig, regime: str = "gaussian") -> dict:
     }
 
 
+def make_gqa_inputs(cfg: DenseConfig, hkv: int) -> dict:
+    """Grouped-query inputs: Q and dO [B, H, N, d], K and V [B, Hkv, N, d], as
+    bfloat16 bits.  One generator (``default_rng(cfg.seed)``) draws float32
+    standard normals for Q, K, V and dO in that order."""
+    rng = np.random.default_rng(cfg.seed)
+    qs = (cfg.B, cfg.H, cfg.N, cfg.d)
+    ks = (cfg.B, hkv, cfg.N, cfg.d)
+    q = rng.standard_normal(qs, dtype=np.float32)
+    k = rng.standard_normal(ks, dtype=np.float32)
+    v = rng.standard_normal(ks, dtype=np.float32)
+    do = rng.standard_normal(qs, dtype=np.float32)
+    return {n: f32_to_bf16_bits(x) for n, x in (("q", q), ("k", k), ("v", v), ("do", do))}
+
+
 # ----------------------------------------------------------------------------
 # Sparse (top-k) inputs
 # ----------------------------------------------------------------------------

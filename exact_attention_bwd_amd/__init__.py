@@ -18,6 +18,7 @@ import torch
 
 __all__ = [
     "attn_fwd", "attn_bwd_preprocess", "attn_bwd", "attn_bwd_workspace_bytes",
+    "attn_fwd_gqa", "attn_bwd_gqa", "attn_bwd_gqa_workspace_bytes",
     "attention_backward", "attn_sparse_fwd", "attn_sparse_bwd", "attn_sparse_bwd_workspace_bytes",
     "lib_path", "AttnError", "version",
 ]
@@ -50,6 +51,14 @@ def _load():
     lib.attn_bwd.restype = i
     lib.attn_bwd_timed.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, vp, vp, vp]
     lib.attn_bwd_timed.restype = i
+    lib.attn_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+    lib.attn_fwd_gqa.restype = i
+    lib.attn_bwd_gqa_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.attn_bwd_gqa_workspace_bytes.restype = sz
+    lib.attn_bwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, f, vp]
+    lib.attn_bwd_gqa.restype = i
+    lib.attn_bwd_gqa_timed.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, f, vp, vp, vp]
+    lib.attn_bwd_gqa_timed.restype = i
     lib.attn_sparse_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
     lib.attn_sparse_fwd.restype = i
     lib.attn_sparse_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
@@ -174,6 +183,65 @@ def attn_bwd(q, k, v, do, lse, D, causal: bool, scale: float | None = None,
         _check(_lib.attn_bwd_timed(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(D), _ptr(dq),
                                    _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, B, H, N, d,
                                    int(bool(causal)), float(scale), _stream(stream), ev0, ev1))
+    return dq, dk, dv
+
+
+def _gqa_shapes(q, k, v):
+    B, H, N, d = _shape4(q, "q")
+    kshape = _shape4(k, "k")
+    _same(kshape, v, "v")
+    if kshape[0] != B or kshape[2:] != (N, d) or kshape[1] < 1 or H % kshape[1] != 0:
+        raise ValueError(f"k / v shape {kshape} does not fit q {tuple(q.shape)} (Hkv must divide H)")
+    return B, H, kshape[1], N, d
+
+
+def attn_fwd_gqa(q, k, v, causal: bool, scale: float | None = None, o=None, lse=None, stream=None):
+    """Grouped-query forward.  q: bf16 [B, H, N, d]; k, v: bf16 [B, Hkv, N, d]
+    with Hkv dividing H.  Returns (o bf16 [B, H, N, d], lse fp32 [B, H, N])."""
+    B, H, Hkv, N, d = _gqa_shapes(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if o is None:
+        o = torch.empty_like(q)
+    _same((B, H, N, d), o, "o")
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _stat(lse, (B, H, N), "lse")
+    _check(_lib.attn_fwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, N, d,
+                             int(bool(causal)), float(scale), _stream(stream)))
+    return o, lse
+
+
+def attn_bwd_gqa_workspace_bytes(B: int, H: int, Hkv: int, N: int, d: int) -> int:
+    return int(_lib.attn_bwd_gqa_workspace_bytes(B, H, Hkv, N, d))
+
+
+def attn_bwd_gqa(q, k, v, do, lse, D, causal: bool, scale: float | None = None,
+                 dq=None, dk=None, dv=None, workspace=None, stream=None, main_events=None):
+    """Grouped-query backward.  Returns (dq [B, H, N, d], dk, dv [B, Hkv, N, d]);
+    dk and dv are summed over the query heads that share each K / V head."""
+    B, H, Hkv, N, d = _gqa_shapes(q, k, v)
+    _same((B, H, N, d), do, "dO")
+    _stat(lse, (B, H, N), "lse")
+    _stat(D, (B, H, N), "D")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _same((B, H, N, d), dq, "dq")
+    _same((B, Hkv, N, d), dk, "dk")
+    _same((B, Hkv, N, d), dv, "dv")
+    need = attn_bwd_gqa_workspace_bytes(B, H, Hkv, N, d)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(D), _ptr(dq), _ptr(dk), _ptr(dv),
+            _ptr(workspace), ws_bytes, B, H, Hkv, N, d, int(bool(causal)), float(scale), _stream(stream))
+    if main_events is None:
+        _check(_lib.attn_bwd_gqa(*args))
+    else:
+        _check(_lib.attn_bwd_gqa_timed(*args, *(ctypes.c_void_p(e) for e in main_events)))
     return dq, dk, dv
 
 

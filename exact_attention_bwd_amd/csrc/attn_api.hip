@@ -45,6 +45,13 @@ attn_status check_shape(int B, int H, int N, int d, bool* empty) {
     return ATTN_OK;
 }
 
+// Grouped-query attention: Hkv key / value heads, each shared by H / Hkv query heads.
+attn_status check_heads(int H, int Hkv) {
+    if (Hkv < 1 || Hkv > H || H % Hkv != 0)
+        return fail(ATTN_ERR_INVALID_ARG, "Hkv=%d does not divide H=%d", Hkv, H);
+    return ATTN_OK;
+}
+
 attn_status check_ptr(const void* p, const char* name, uintptr_t align) {
     if (p == nullptr) return fail(ATTN_ERR_INVALID_ARG, "%s is NULL", name);
     if (!aligned(p, align)) return fail(ATTN_ERR_INVALID_ARG, "%s is not %u-byte aligned", name, (unsigned)align);
@@ -61,20 +68,26 @@ attn_status check_ptr(const void* p, const char* name, uintptr_t align) {
 
 extern "C" {
 
-attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                     int H, int N, int d, int causal, float scale, void* stream) {
+attn_status attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                         int H, int Hkv, int N, int d, int causal, float scale, void* stream) {
     bool empty = false;
     CHECK(check_shape(B, H, N, d, &empty));
     if (!isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "scale is not finite");
     if (empty) return ok();
+    CHECK(check_heads(H, Hkv));
     CHECK(check_ptr(q, "q", 16));
     CHECK(check_ptr(k, "k", 16));
     CHECK(check_ptr(v, "v", 16));
     CHECK(check_ptr(o, "o", 16));
     CHECK(check_ptr(lse, "lse", 4));
-    return hip_status(attn::launch_fwd(q, k, v, o, lse, B * H, N, d, causal != 0, scale,
+    return hip_status(attn::launch_fwd(q, k, v, o, lse, B * H, H, H / Hkv, N, d, causal != 0, scale,
                                        (hipStream_t)stream),
                       "attn_fwd launch");
+}
+
+attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                     int H, int N, int d, int causal, float scale, void* stream) {
+    return attn_fwd_gqa(q, k, v, o, lse, B, H, H, N, d, causal, scale, stream);
 }
 
 attn_status attn_bwd_preprocess(const void* o, const void* dO, float* D, int B, int H, int N,
@@ -90,20 +103,27 @@ attn_status attn_bwd_preprocess(const void* o, const void* dO, float* D, int B, 
                       "attn_bwd_preprocess launch");
 }
 
-size_t attn_bwd_workspace_bytes(int B, int H, int N, int d) {
+size_t attn_bwd_gqa_workspace_bytes(int B, int H, int Hkv, int N, int d) {
     bool empty = false;
     if (check_shape(B, H, N, d, &empty) != ATTN_OK || empty) return 0;
-    return attn::bwd_workspace_bytes(B * H, N, d);
+    if (check_heads(H, Hkv) != ATTN_OK) return 0;
+    return attn::bwd_workspace_bytes(B * H, H / Hkv, N, d);
 }
 
-attn_status attn_bwd_timed(const void* q, const void* k, const void* v, const void* dO,
-                     const float* lse, const float* D, void* dq, void* dk, void* dv,
-                     void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
-                     int causal, float scale, void* stream, void* main_start, void* main_stop) {
+size_t attn_bwd_workspace_bytes(int B, int H, int N, int d) {
+    return attn_bwd_gqa_workspace_bytes(B, H, H, N, d);
+}
+
+attn_status attn_bwd_gqa_timed(const void* q, const void* k, const void* v, const void* dO,
+                               const float* lse, const float* D, void* dq, void* dk, void* dv,
+                               void* workspace, size_t workspace_bytes, int B, int H, int Hkv, int N,
+                               int d, int causal, float scale, void* stream, void* main_start,
+                               void* main_stop) {
     bool empty = false;
     CHECK(check_shape(B, H, N, d, &empty));
     if (!isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "scale is not finite");
     if (empty) return ok();
+    CHECK(check_heads(H, Hkv));
     CHECK(check_ptr(q, "q", 16));
     CHECK(check_ptr(k, "k", 16));
     CHECK(check_ptr(v, "v", 16));
@@ -114,21 +134,37 @@ attn_status attn_bwd_timed(const void* q, const void* k, const void* v, const vo
     CHECK(check_ptr(dk, "dk", 16));
     CHECK(check_ptr(dv, "dv", 16));
     CHECK(check_ptr(workspace, "workspace", 16));
-    const size_t need = attn::bwd_workspace_bytes(B * H, N, d);
+    const size_t need = attn::bwd_workspace_bytes(B * H, H / Hkv, N, d);
     if (workspace_bytes < need)
         return fail(ATTN_ERR_WORKSPACE, "workspace is %zu bytes, %zu needed", workspace_bytes, need);
-    return hip_status(attn::launch_bwd(q, k, v, dO, lse, D, dq, dk, dv, workspace, B * H, N, d,
-                                       causal != 0, scale, (hipStream_t)stream,
+    return hip_status(attn::launch_bwd(q, k, v, dO, lse, D, dq, dk, dv, workspace, B * H, H, H / Hkv,
+                                       N, d, causal != 0, scale, (hipStream_t)stream,
                                        (hipEvent_t)main_start, (hipEvent_t)main_stop),
                       "attn_bwd launch");
+}
+
+attn_status attn_bwd_gqa(const void* q, const void* k, const void* v, const void* dO,
+                         const float* lse, const float* D, void* dq, void* dk, void* dv,
+                         void* workspace, size_t workspace_bytes, int B, int H, int Hkv, int N,
+                         int d, int causal, float scale, void* stream) {
+    return attn_bwd_gqa_timed(q, k, v, dO, lse, D, dq, dk, dv, workspace, workspace_bytes, B, H, Hkv,
+                              N, d, causal, scale, stream, nullptr, nullptr);
+}
+
+attn_status attn_bwd_timed(const void* q, const void* k, const void* v, const void* dO,
+                           const float* lse, const float* D, void* dq, void* dk, void* dv,
+                           void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                           int causal, float scale, void* stream, void* main_start, void* main_stop) {
+    return attn_bwd_gqa_timed(q, k, v, dO, lse, D, dq, dk, dv, workspace, workspace_bytes, B, H, H, N,
+                              d, causal, scale, stream, main_start, main_stop);
 }
 
 attn_status attn_bwd(const void* q, const void* k, const void* v, const void* dO,
                      const float* lse, const float* D, void* dq, void* dk, void* dv,
                      void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
                      int causal, float scale, void* stream) {
-    return attn_bwd_timed(q, k, v, dO, lse, D, dq, dk, dv, workspace, workspace_bytes, B, H, N, d,
-                          causal, scale, stream, nullptr, nullptr);
+    return attn_bwd_gqa_timed(q, k, v, dO, lse, D, dq, dk, dv, workspace, workspace_bytes, B, H, H, N,
+                              d, causal, scale, stream, nullptr, nullptr);
 }
 
 // ---------------------------------------------------------------------------

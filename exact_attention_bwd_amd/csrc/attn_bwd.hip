@@ -174,7 +174,7 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                      const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                      const float* __restrict__ Lb, const float* __restrict__ Dp,
                      __bf16* __restrict__ dSw, __bf16* __restrict__ Kimg, __bf16* __restrict__ dK,
-                     __bf16* __restrict__ dV, int BH, int N, int n_pad, float scale) {
+                     __bf16* __restrict__ dV, int BH, int H, int G, int N, int n_pad, float scale) {
     using S = Smem<HD>;
     constexpr int KSD = HD / 16;                 // k steps over the head dim
     constexpr int DB = HD / 32;                  // 32-wide blocks of the head dim
@@ -194,15 +194,14 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const int tc = (N + BC - 1) / BC;
     const int tr_count = (N + BR - 1) / BR;
     const int logical = xcd_remap(blockIdx.x, BH * tc);
-    const int bh = logical / tc;
+    const int bh = logical / tc;                 // K / V head (BH = B * H / G of them)
     const int j = logical % tc;                  // heavy (small j) first when causal
     const int k0 = j * BC;
 
-    const size_t head = (size_t)bh * N * HD;
-    const __bf16* Qh = Q + head;
-    const __bf16* dOh = dO + head;
-    const float* Lbh = Lb + (size_t)bh * n_pad;
-    const float* Dph = Dp + (size_t)bh * n_pad;
+    const size_t head = (size_t)bh * N * HD;     // K, V, dK, dV
+    // grouped-query attention: the G query heads hq0 .. hq0 + G - 1 share this
+    // K / V head; their contributions to dK_j and dV_j are summed in registers
+    const int hq0 = (bh / (H / G)) * H + (bh % (H / G)) * G;
 
     __bf16* const QB = reinterpret_cast<__bf16*>(smem + S::off_q);   // Q buffers; dO at +2 tiles
     __bf16* const KB = reinterpret_cast<__bf16*>(smem + S::off_k);   // K; V at +BC*HD
@@ -239,22 +238,25 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     int vo_q[BR * (HD / 8) / 64 / NW], vo_k[BC * (HD / 8) / 64 / NW];
     stage_offsets<HD, BR, NW>(vo_q, w, lane);
     stage_offsets<HD, BC, NW>(vo_k, w, lane);
-    auto stage_tile = [&](int it, int buf) {
+    auto stage_tile = [&](int gq, int it, int buf) {
         const int q0 = it * BR;
         const int bytes = min(N - q0, BR) * ROWB;
-        stage_rows_b<HD, BR, NW>(make_rsrc(Qh + (size_t)q0 * HD, bytes), vo_q,
+        const size_t qhd = (size_t)(hq0 + gq) * N * HD;
+        const size_t qst = (size_t)(hq0 + gq) * n_pad;
+        stage_rows_b<HD, BR, NW>(make_rsrc(Q + qhd + (size_t)q0 * HD, bytes), vo_q,
                                  smem + S::off_q + buf * S::TILE, w);
-        stage_rows_b<HD, BR, NW>(make_rsrc(dOh + (size_t)q0 * HD, bytes), vo_q,
+        stage_rows_b<HD, BR, NW>(make_rsrc(dO + qhd + (size_t)q0 * HD, bytes), vo_q,
                                  smem + S::off_do + buf * S::TILE, w);
-        if (w == 0) bdma4(make_rsrc(Lbh + q0, BR * 4), lane * 4, smem + S::off_l + buf * BR * 4);
-        if (w == 1) bdma4(make_rsrc(Dph + q0, BR * 4), lane * 4, smem + S::off_d + buf * BR * 4);
+        if (w == 0) bdma4(make_rsrc(Lb + qst + q0, BR * 4), lane * 4, smem + S::off_l + buf * BR * 4);
+        if (w == 1) bdma4(make_rsrc(Dp + qst + q0, BR * 4), lane * 4, smem + S::off_d + buf * BR * 4);
     };
     {
         const int bytes = min(N - k0, BC) * ROWB;
         stage_rows_b<HD, BC, NW>(make_rsrc(K + head + (size_t)k0 * HD, bytes), vo_k, smem + S::off_k, w);
         stage_rows_b<HD, BC, NW>(make_rsrc(V + head + (size_t)k0 * HD, bytes), vo_k, smem + S::off_v, w);
     }
-    stage_tile(it0, 0);
+    const int nt = tr_count - it0;               // query tiles per query head
+    stage_tile(0, it0, 0);
     __syncthreads();
 
     // ---- K_j image for the dQ kernel: 2 * DB * 8 blocks of 1 KiB, spread over
@@ -285,9 +287,11 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const float sl2 = scale * kLog2e;
     const int key_lane = k0 + kw * 32 + l32;     // this lane's key (accumulator column)
 
-    for (int it = it0, buf = 0; it < tr_count; ++it, buf ^= 1) {
+    for (int step = 0, buf = 0; step < G * nt; ++step, buf ^= 1) {
+        const int gq = step / nt, it = it0 + step % nt;
         const int q0 = it * BR;
-        if (it + 1 < tr_count) stage_tile(it + 1, buf ^ 1);     // lands during this iteration
+        if (step + 1 < G * nt)                   // lands during this iteration
+            stage_tile((step + 1) / nt, it0 + (step + 1) % nt, buf ^ 1);
         const __bf16* Qs = QB + buf * TILE_EL;
         const __bf16* dOs = Qs + 2 * TILE_EL;
         const float* Ls = LB + buf * BR;
@@ -352,7 +356,7 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         // not also wait for them
         __syncthreads();
         const __amdgpu_buffer_rsrc_t dsr =
-            make_rsrc(dSw + dst_tile(bh, it, j, tr_count, tc), DST_EL * 2);
+            make_rsrc(dSw + dst_tile(hq0 + gq, it, j, tr_count, tc), DST_EL * 2);
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ds0), dsr,
                                                dst_run(qh, kw >> 1, kw & 1, 0) + lane * 16, 0, 0);
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ds1), dsr,
@@ -419,7 +423,7 @@ void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict_
                          const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                          const float* __restrict__ Lb, const float* __restrict__ Dp,
                          __bf16* __restrict__ dSw, __bf16* __restrict__ Kimg,
-                         __bf16* __restrict__ dK, __bf16* __restrict__ dV, int BH, int N,
+                         __bf16* __restrict__ dK, __bf16* __restrict__ dV, int BH, int H, int G, int N,
                          int n_pad, float scale) {
     constexpr int HD = 128;
     using S = Smem2;
@@ -464,11 +468,10 @@ void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict_
     const int k0 = j * BC2;
     const int kw0 = k0 + 64 * w;                 // this wave's first key
 
-    const size_t head = (size_t)bh * N * HD;
-    const __bf16* Qh = Q + head;
-    const __bf16* dOh = dO + head;
-    const float* Lbh = Lb + (size_t)bh * n_pad;
-    const float* Dph = Dp + (size_t)bh * n_pad;
+    const size_t head = (size_t)bh * N * HD;     // K, V, dK, dV (BH = B * H / G heads)
+    // grouped-query attention: the G query heads hq0 .. hq0 + G - 1 share this
+    // K / V head; their contributions to dK_j and dV_j are summed in registers
+    const int hq0 = (bh / (H / G)) * H + (bh % (H / G)) * G;
     const __bf16* VS = reinterpret_cast<const __bf16*>(smem + S::off_v);
     const __bf16* KS = reinterpret_cast<const __bf16*>(smem + S::off_kstage);
 
@@ -521,20 +524,23 @@ void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict_
     }
     __syncthreads();                             // K staging consumed
 
-    auto stage_tile = [&](int it, int buf) {
+    auto stage_tile = [&](int gq, int it, int buf) {
         const int q0 = it * BR;
         const int bytes = min(N - q0, BR) * ROWB;
-        stage_rows_b<HD, BR, NW2>(make_rsrc(Qh + (size_t)q0 * HD, bytes), vo_q,
+        const size_t qhd = (size_t)(hq0 + gq) * N * HD;
+        const size_t qst = (size_t)(hq0 + gq) * n_pad;
+        stage_rows_b<HD, BR, NW2>(make_rsrc(Q + qhd + (size_t)q0 * HD, bytes), vo_q,
                                   smem + S::off_q + buf * S::TILE, w);
-        stage_rows_b<HD, BR, NW2>(make_rsrc(dOh + (size_t)q0 * HD, bytes), vo_q,
+        stage_rows_b<HD, BR, NW2>(make_rsrc(dO + qhd + (size_t)q0 * HD, bytes), vo_q,
                                   smem + S::off_do + buf * S::TILE, w);
-        if (w == 0) bdma4(make_rsrc(Lbh + q0, BR * 4), lane * 4, smem + S::off_l + buf * BR * 4);
-        if (w == 1) bdma4(make_rsrc(Dph + q0, BR * 4), lane * 4, smem + S::off_d + buf * BR * 4);
+        if (w == 0) bdma4(make_rsrc(Lb + qst + q0, BR * 4), lane * 4, smem + S::off_l + buf * BR * 4);
+        if (w == 1) bdma4(make_rsrc(Dp + qst + q0, BR * 4), lane * 4, smem + S::off_d + buf * BR * 4);
     };
     // query tiles are walked from the last one down to the diagonal: the
     // workgroups of one head then read the same Q_i / dO_i at the same time,
     // and the shared L2 serves all but the first
-    stage_tile(tr_count - 1, 0);
+    const int nt = tr_count - it0;               // query tiles per query head
+    stage_tile(0, tr_count - 1, 0);
     __syncthreads();
 
     f32x16 dv[2][DB], dk[2][DB];
@@ -552,16 +558,18 @@ void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict_
     // block 1 at + 8 KiB
     const uint32_t aV = lds_addr(VS) + (uint32_t)((64 * w * HD + ob0) * 2);
 
-    for (int it = tr_count - 1, buf = 0; it >= it0; --it, buf ^= 1) {
+    for (int step = 0, buf = 0; step < G * nt; ++step, buf ^= 1) {
+        const int gq = step / nt, it = tr_count - 1 - step % nt;
         const int q0 = it * BR;
-        if (it - 1 >= it0) stage_tile(it - 1, buf ^ 1);     // lands during this iteration
+        if (step + 1 < G * nt)                   // lands during this iteration
+            stage_tile((step + 1) / nt, tr_count - 1 - (step + 1) % nt, buf ^ 1);
         const __bf16* Qs = reinterpret_cast<const __bf16*>(smem + S::off_q) + buf * TILE_EL;
         const __bf16* dOs = reinterpret_cast<const __bf16*>(smem + S::off_do) + buf * TILE_EL;
         const float* Ls = reinterpret_cast<const float*>(smem + S::off_l) + buf * BR;
         const float* Ds = reinterpret_cast<const float*>(smem + S::off_d) + buf * BR;
         // dS stores go nowhere (buffer records 0) for a 128-key half past N
         const __amdgpu_buffer_rsrc_t dsr =
-            make_rsrc(dSw + dst_tile(bh, it, min(jst, tc - 1), tr_count, tc), jst < tc ? DST_EL * 2 : 0);
+            make_rsrc(dSw + dst_tile(hq0 + gq, it, min(jst, tc - 1), tr_count, tc), jst < tc ? DST_EL * 2 : 0);
         // transposing-read bases of this tile: Q buffer + lane offset for the
         // 4 column blocks x 2 row halves; dO, the row half qb and k4 are
         // immediate offsets
@@ -769,7 +777,7 @@ constexpr int QW = 4;                            // waves per dQ workgroup
 template <int HD, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(QW * 64, QW * 64)))
 void bwd_dq_kernel(const __bf16* __restrict__ Kimg, const __bf16* __restrict__ dSw,
-                   __bf16* __restrict__ dQ, int BH, int N, float scale) {
+                   __bf16* __restrict__ dQ, int BH, int H, int G, int N, float scale) {
     constexpr int DB = HD / 32;
     constexpr int TQ = 4 * DB / QW;              // 32-row query blocks per wave (4 or 2)
     constexpr int DS_B = DST_EL * 2;             // one dS tile (bytes)
@@ -834,7 +842,7 @@ void bwd_dq_kernel(const __bf16* __restrict__ Kimg, const __bf16* __restrict__ d
     // step's own vmcnt wait covers them
     const uint32_t kvo = (uint32_t)((db * KS * 64 + lane) * 16);
     auto load_k = [&](int jj, bf16x8* kb) {
-        const __bf16* kt = Kimg + kimg_tile(bh, jj, tc, HD);
+        const __bf16* kt = Kimg + kimg_tile(kv_head(bh, H, G), jj, tc, HD);
         static_for<0, KS>([&](auto ksI) {
             constexpr int ks = decltype(ksI)::value;
             gload16<(ks & 3) * 1024>(kb[ks], kt, kvo + (ks >> 2) * 4096);
@@ -933,22 +941,25 @@ hipError_t launch_bwd_preprocess(const void* o, const void* dO, float* D, int BH
 }
 
 // Workspace: [Lb BH x n_pad fp32][D BH x n_pad fp32][dS tiles BH x T_r x T_c
-// x (BC x BR) bf16][K image BH x T_c x (BC x d) bf16].  Every dS tile the dQ
-// kernel reads is written by the dK/dV kernel first (causal: exactly the tiles
-// with j <= i / 2), and so is every K image tile.
+// x (BC x BR) bf16][K image BH / G x T_c x (BC x d) bf16] for BH query heads
+// and BH / G key / value heads.  Every dS tile the dQ kernel reads is written
+// by the dK/dV kernel first (causal: exactly the tiles with j <= i / 2), and so
+// is every K image tile.
 static size_t n_pad_of(int N) { return (size_t)((N + bwd::BR - 1) / bwd::BR) * bwd::BR; }
 
-size_t bwd_workspace_bytes(int BH, int N, int d) {
+size_t bwd_workspace_bytes(int BH, int G, int N, int d) {
     const size_t rows = (size_t)BH * n_pad_of(N);
     const size_t tr = (N + bwd::BR - 1) / bwd::BR, tc = (N + bwd::BC - 1) / bwd::BC;
     return 2 * rows * sizeof(float) + (size_t)BH * tr * tc * bwd::DST_EL * 2 +
-           (size_t)BH * tc * bwd::BC * d * 2;
+           (size_t)(BH / G) * tc * bwd::BC * d * 2;
 }
 
+// BHkv = B * H / G key / value heads (the dK/dV grid)
 template <int HD, bool CAUSAL>
 static hipError_t launch_dkdv(const void* q, const void* k, const void* v, const void* dO,
                               const float* Lb, const float* Dp, __bf16* dSw, __bf16* kimg, void* dk,
-                              void* dv, int BH, int N, int n_pad, float scale, hipStream_t stream) {
+                              void* dv, int BHkv, int H, int G, int N, int n_pad, float scale,
+                              hipStream_t stream) {
 #ifndef ATTN_DKDV_W32
     if (HD == 128) {
         using S2 = bwd::Smem2;
@@ -957,9 +968,9 @@ static hipError_t launch_dkdv(const void* q, const void* k, const void* v, const
                                            hipFuncAttributeMaxDynamicSharedMemorySize, S2::bytes);
         if (e != hipSuccess) return e;
         const int tc2 = (N + bwd::BC2 - 1) / bwd::BC2;
-        hipLaunchKernelGGL(kern, dim3(BH * tc2), dim3(bwd::NW2 * 64), S2::bytes, stream,
+        hipLaunchKernelGGL(kern, dim3(BHkv * tc2), dim3(bwd::NW2 * 64), S2::bytes, stream,
                            (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dO,
-                           Lb, Dp, dSw, kimg, (__bf16*)dk, (__bf16*)dv, BH, N, n_pad, scale);
+                           Lb, Dp, dSw, kimg, (__bf16*)dk, (__bf16*)dv, BHkv, H, G, N, n_pad, scale);
         return hipGetLastError();
     }
 #endif
@@ -969,38 +980,38 @@ static hipError_t launch_dkdv(const void* q, const void* k, const void* v, const
                                        hipFuncAttributeMaxDynamicSharedMemorySize, S::bytes);
     if (e != hipSuccess) return e;
     const int tc = (N + bwd::BC - 1) / bwd::BC;
-    hipLaunchKernelGGL(kern, dim3(BH * tc), dim3(bwd::NT), S::bytes, stream, (const __bf16*)q,
+    hipLaunchKernelGGL(kern, dim3(BHkv * tc), dim3(bwd::NT), S::bytes, stream, (const __bf16*)q,
                        (const __bf16*)k, (const __bf16*)v, (const __bf16*)dO, Lb, Dp, dSw, kimg,
-                       (__bf16*)dk, (__bf16*)dv, BH, N, n_pad, scale);
+                       (__bf16*)dk, (__bf16*)dv, BHkv, H, G, N, n_pad, scale);
     return hipGetLastError();
 }
 
 template <int HD, bool CAUSAL>
-static hipError_t launch_dq(const __bf16* kimg, const __bf16* dSw, void* dq, int BH, int N,
-                            float scale, hipStream_t stream) {
+static hipError_t launch_dq(const __bf16* kimg, const __bf16* dSw, void* dq, int BH, int H, int G,
+                            int N, float scale, hipStream_t stream) {
     const int tr = (N + bwd::BR - 1) / bwd::BR;
     hipLaunchKernelGGL((bwd::bwd_dq_kernel<HD, CAUSAL>), dim3(BH * ((tr + 1) / 2)), dim3(bwd::QW * 64), 0, stream,
-                       kimg, dSw, (__bf16*)dq, BH, N, scale);
+                       kimg, dSw, (__bf16*)dq, BH, H, G, N, scale);
     return hipGetLastError();
 }
 
 template <int HD, bool CAUSAL>
 static hipError_t launch_pair(const void* q, const void* k, const void* v, const void* dO,
                               const float* Lb, const float* Dp, __bf16* dSw, __bf16* kimg, void* dq,
-                              void* dk, void* dv, int BH, int N, int n_pad, float scale,
+                              void* dk, void* dv, int BH, int H, int G, int N, int n_pad, float scale,
                               hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
     hipError_t e;
     if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
-    e = launch_dkdv<HD, CAUSAL>(q, k, v, dO, Lb, Dp, dSw, kimg, dk, dv, BH, N, n_pad, scale, stream);
+    e = launch_dkdv<HD, CAUSAL>(q, k, v, dO, Lb, Dp, dSw, kimg, dk, dv, BH / G, H, G, N, n_pad, scale, stream);
     if (e != hipSuccess) return e;
     if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
-    return launch_dq<HD, CAUSAL>(kimg, dSw, dq, BH, N, scale, stream);
+    return launch_dq<HD, CAUSAL>(kimg, dSw, dq, BH, H, G, N, scale, stream);
 }
 
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* dO, const float* lse,
-                      const float* D, void* dq, void* dk, void* dv, void* workspace, int BH, int N,
-                      int d, bool causal, float scale, hipStream_t stream, hipEvent_t main_start,
-                      hipEvent_t main_stop) {
+                      const float* D, void* dq, void* dk, void* dv, void* workspace, int BH, int H,
+                      int G, int N, int d, bool causal, float scale, hipStream_t stream,
+                      hipEvent_t main_start, hipEvent_t main_stop) {
     if ((long long)BH * N == 0) return hipSuccess;
     const int n_pad = (int)n_pad_of(N);
     const size_t rows = (size_t)BH * n_pad;
@@ -1014,10 +1025,10 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* d
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (d == 128)
-        return causal ? launch_pair<128, true>(q, k, v, dO, Lb, Dp, dSw, kimg, dq, dk, dv, BH, N, n_pad, scale, stream, main_start, main_stop)
-                      : launch_pair<128, false>(q, k, v, dO, Lb, Dp, dSw, kimg, dq, dk, dv, BH, N, n_pad, scale, stream, main_start, main_stop);
-    return causal ? launch_pair<64, true>(q, k, v, dO, Lb, Dp, dSw, kimg, dq, dk, dv, BH, N, n_pad, scale, stream, main_start, main_stop)
-                  : launch_pair<64, false>(q, k, v, dO, Lb, Dp, dSw, kimg, dq, dk, dv, BH, N, n_pad, scale, stream, main_start, main_stop);
+        return causal ? launch_pair<128, true>(q, k, v, dO, Lb, Dp, dSw, kimg, dq, dk, dv, BH, H, G, N, n_pad, scale, stream, main_start, main_stop)
+                      : launch_pair<128, false>(q, k, v, dO, Lb, Dp, dSw, kimg, dq, dk, dv, BH, H, G, N, n_pad, scale, stream, main_start, main_stop);
+    return causal ? launch_pair<64, true>(q, k, v, dO, Lb, Dp, dSw, kimg, dq, dk, dv, BH, H, G, N, n_pad, scale, stream, main_start, main_stop)
+                  : launch_pair<64, false>(q, k, v, dO, Lb, Dp, dSw, kimg, dq, dk, dv, BH, H, G, N, n_pad, scale, stream, main_start, main_stop);
 }
 
 }  // namespace attn

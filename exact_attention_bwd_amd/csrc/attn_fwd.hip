@@ -100,7 +100,7 @@ template <int HD, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                 const __bf16* __restrict__ V, __bf16* __restrict__ O, float* __restrict__ Lse,
-                int BH, int N, float scale) {
+                int BH, int H, int G, int N, float scale) {
     using S = Smem<HD>;
     constexpr int KSD = HD / 16;
     constexpr int DB = HD / 32;
@@ -120,8 +120,10 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 
     const size_t head = (size_t)bh * N * HD;
     const __bf16* Qh = Q + head;
-    const __bf16* Kh = K + head;
-    const __bf16* Vh = V + head;
+    // grouped-query attention: query head h of a batch reads K / V head h / G
+    const size_t kvhead = (size_t)kv_head(bh, H, G) * N * HD;
+    const __bf16* Kh = K + kvhead;
+    const __bf16* Vh = V + kvhead;
 
     // this lane's query row (the accumulator column of S^T and O^T)
     const int qrow = q0 + w * 32 + l32;
@@ -379,11 +381,11 @@ template <bool CAUSAL, int RB>
 __global__ __attribute__((amdgpu_flat_work_group_size(512 / RB, 512 / RB), amdgpu_waves_per_eu(3 - RB, 3 - RB)))
 void fwd_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                     const __bf16* __restrict__ V, __bf16* __restrict__ O, float* __restrict__ Lse,
-                    int BH, int N, float scale) {
+                    int BH, int H, int G, int N, float scale) {
     constexpr int HD = 128;
     constexpr int NW = 8 / RB;                   // waves per workgroup
     constexpr int EPT = 32 * RB;                 // softmax elements per lane per key tile
-    constexpr int H = EPT / 2;                   // of which key block 0
+    constexpr int EH = EPT / 2;                  // of which key block 0
     constexpr int NS = 16 * RB;                  // MFMA slots per phase
     using SC = FwdSched;
     using S = WSmem;
@@ -425,8 +427,10 @@ void fwd_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const int qrows = min(N - q0, WBM);
     const int qw = 32 * RB * w;                  // this wave's first row in the tile
     const size_t head = (size_t)bh * N * HD;
-    const __bf16* Kh = K + head;
-    const __bf16* Vh = V + head;
+    // grouped-query attention: query head h of a batch reads K / V head h / G
+    const size_t kvhead = (size_t)kv_head(bh, H, G) * N * HD;
+    const __bf16* Kh = K + kvhead;
+    const __bf16* Vh = V + kvhead;
     const int T = CAUSAL ? (q0 + qrows - 1) / BN + 1 : (N + BN - 1) / BN;   // key tiles
 
     // Q rows of this lane as B operands of S^T: Q[qw + 32 qb + l32][16 ks + 8 g ..]
@@ -628,7 +632,7 @@ void fwd_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         pmax[qb] = max8(max8(max8(max8(-__builtin_inff(), sa[qb][0], 0), sa[qb][0], 1), sa[qb][1], 0), sa[qb][1], 1);
         combine(qb);
     }
-    static_for<0, H>([&](auto eI) __attribute__((always_inline)) { elem(sa, eI); });
+    static_for<0, EH>([&](auto eI) __attribute__((always_inline)) { elem(sa, eI); });
 
     // ---- main loop.  Slot rules (B_t = the barrier of iteration t):
     //  * iteration t reads K_{t+1} (S phase; its first D operands are issued
@@ -655,8 +659,8 @@ void fwd_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
             }
             if constexpr (ks == 0) mfma_q0(sn[qb][kb], kop[n], qa[qb][ks]);
             else mfma_q(sn[qb][kb], kop[n], qa[qb][ks]);
-            elem_exp(sc, std::integral_constant<int, H + m>{});
-            if constexpr (m > 0) elem_sum(std::integral_constant<int, H + m - 1>{});
+            elem_exp(sc, std::integral_constant<int, EH + m>{});
+            if constexpr (m > 0) elem_sum(std::integral_constant<int, EH + m - 1>{});
             // mask and row max of S(t+1), key block 0 (its last products: the
             // slots before 8 RB)
             if constexpr (m == 8 * RB) {
@@ -762,18 +766,18 @@ void fwd_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 
 template <int HD, bool CAUSAL>
 static hipError_t launch_fwd_t(const void* q, const void* k, const void* v, void* o, float* lse,
-                               int BH, int N, float scale, hipStream_t stream) {
+                               int BH, int H, int G, int N, float scale, hipStream_t stream) {
     using S = fwd::Smem<HD>;
     auto kern = fwd::fwd_kernel<HD, CAUSAL>;
     const int tq = (N + fwd::BM - 1) / fwd::BM;
     hipLaunchKernelGGL(kern, dim3(BH * tq), dim3(fwd::NT), S::bytes, stream, (const __bf16*)q,
-                       (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, BH, N, scale);
+                       (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, BH, H, G, N, scale);
     return hipGetLastError();
 }
 
 template <bool CAUSAL>
 static hipError_t launch_fwd_w64(const void* q, const void* k, const void* v, void* o, float* lse,
-                                 int BH, int N, float scale, hipStream_t stream) {
+                                 int BH, int H, int G, int N, float scale, hipStream_t stream) {
     using S = fwd::WSmem;
     constexpr int RB = FWD_RB;
     auto kern = fwd::fwd_w64_kernel<CAUSAL, RB>;
@@ -781,18 +785,18 @@ static hipError_t launch_fwd_w64(const void* q, const void* k, const void* v, vo
     if (e != hipSuccess) return e;
     const int tq = (N + fwd::WBM - 1) / fwd::WBM;
     hipLaunchKernelGGL(kern, dim3(BH * tq), dim3(512 / RB), S::bytes, stream, (const __bf16*)q,
-                       (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, BH, N, scale);
+                       (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, BH, H, G, N, scale);
     return hipGetLastError();
 }
 
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
-                      int N, int d, bool causal, float scale, hipStream_t stream) {
+                      int H, int G, int N, int d, bool causal, float scale, hipStream_t stream) {
     if ((long long)BH * N == 0) return hipSuccess;
     if (d == 128)
-        return causal ? launch_fwd_w64<true>(q, k, v, o, lse, BH, N, scale, stream)
-                      : launch_fwd_w64<false>(q, k, v, o, lse, BH, N, scale, stream);
-    return causal ? launch_fwd_t<64, true>(q, k, v, o, lse, BH, N, scale, stream)
-                  : launch_fwd_t<64, false>(q, k, v, o, lse, BH, N, scale, stream);
+        return causal ? launch_fwd_w64<true>(q, k, v, o, lse, BH, H, G, N, scale, stream)
+                      : launch_fwd_w64<false>(q, k, v, o, lse, BH, H, G, N, scale, stream);
+    return causal ? launch_fwd_t<64, true>(q, k, v, o, lse, BH, H, G, N, scale, stream)
+                  : launch_fwd_t<64, false>(q, k, v, o, lse, BH, H, G, N, scale, stream);
 }
 
 }  // namespace attn

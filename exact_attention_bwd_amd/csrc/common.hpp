@@ -148,4 +148,11 @@ __device__ __forceinline__ int xcd_remap(int hw, int total) {
     return x * q + (x < r ? x : r) + local;
 }
 
+// Grouped-query attention: flattened query head bh = b * H + h reads the
+// key / value head b * (H / G) + h / G (G query heads per K / V head; G = 1 is
+// ordinary multi-head attention).
+__device__ __forceinline__ int kv_head(int bh, int H, int G) {
+    return (bh / H) * (H / G) + (bh % H) / G;
+}
+
 }  // namespace attn

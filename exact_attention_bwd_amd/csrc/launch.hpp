@@ -8,17 +8,18 @@
 
 namespace attn {
 
+// BH = B * H query heads; G query heads share each K / V head (H % G == 0)
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
-                      int N, int d, bool causal, float scale, hipStream_t stream);
+                      int H, int G, int N, int d, bool causal, float scale, hipStream_t stream);
 
 hipError_t launch_bwd_preprocess(const void* o, const void* dO, float* D, int BH, int N, int d,
                                  hipStream_t stream);
 
-size_t bwd_workspace_bytes(int BH, int N, int d);
+size_t bwd_workspace_bytes(int BH, int G, int N, int d);
 
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* dO, const float* lse,
-                      const float* D, void* dq, void* dk, void* dv, void* workspace, int BH, int N,
-                      int d, bool causal, float scale, hipStream_t stream,
+                      const float* D, void* dq, void* dk, void* dv, void* workspace, int BH, int H,
+                      int G, int N, int d, bool causal, float scale, hipStream_t stream,
                       hipEvent_t main_start = nullptr, hipEvent_t main_stop = nullptr);
 
 // Top-k sparse attention (d_qk = 576, d_v = 512, heads in groups of 64).

@@ -117,6 +117,44 @@ attn_status attn_bwd_timed(const void* q, const void* k, const void* v, const vo
 
 /*
  * ---------------------------------------------------------------------------
+ * Grouped-query attention (GQA; MQA when Hkv = 1): Hkv key / value heads, each
+ * shared by G = H / Hkv consecutive query heads, the dense counterpart of the
+ * shared K/V head of the sparse path below (cudnn-frontend PR #684, DSA: all
+ * query heads attend through one K/V head, and dK, dV are sums over heads).
+ * Query head h of batch b reads K / V head h / G of batch b:
+ *     S_h = scale * Q_h K_{h/G}^T + M,   O_h = softmax(S_h) V_{h/G}
+ * and the backward forms dQ_h as for dense attention and
+ *     dK_c = sum over the query heads h with h / G = c of scale * dS_h^T Q_h,
+ *     dV_c = sum over the same heads of P_h^T dO_h.
+ * Shapes: q, o, dO, dq  [B, H, N, d];  k, v, dk, dv  [B, Hkv, N, d];
+ * lse, D fp32 [B, H, N].  Hkv must divide H (ATTN_ERR_INVALID_ARG otherwise);
+ * everything else as for attn_fwd / attn_bwd, which are these calls with
+ * Hkv = H.  The per-head sums of dK and dV are accumulated in registers in a
+ * fixed order (no atomics): results are bitwise reproducible.
+ */
+attn_status attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                         int H, int Hkv, int N, int d, int causal, float scale, void* stream);
+
+/* Workspace of attn_bwd_gqa: as attn_bwd_workspace_bytes(B, H, N, d) but with
+ * the K image sized for the Hkv key / value heads.  0 for invalid shapes. */
+size_t attn_bwd_gqa_workspace_bytes(int B, int H, int Hkv, int N, int d);
+
+/* Grouped-query backward: lse, D and dO per query head, dk / dv per K / V head. */
+attn_status attn_bwd_gqa(const void* q, const void* k, const void* v, const void* dO,
+                         const float* lse, const float* D, void* dq, void* dk, void* dv,
+                         void* workspace, size_t workspace_bytes, int B, int H, int Hkv, int N,
+                         int d, int causal, float scale, void* stream);
+
+/* attn_bwd_gqa with the dK/dV kernel bracketed by main_start / main_stop, as
+ * attn_bwd_timed. */
+attn_status attn_bwd_gqa_timed(const void* q, const void* k, const void* v, const void* dO,
+                               const float* lse, const float* D, void* dq, void* dk, void* dv,
+                               void* workspace, size_t workspace_bytes, int B, int H, int Hkv, int N,
+                               int d, int causal, float scale, void* stream, void* main_start,
+                               void* main_stop);
+
+/*
+ * ---------------------------------------------------------------------------
  * Top-k sparse attention (cudnn-frontend PR #684, "Improve performance of
  * SM100 DSA backward kernel": DSA attention with one shared K/V head).
  * Query row i attends, for every head, to the keys its index list names:

@@ -46,6 +46,7 @@ __all__ = [
     "causal_allowed", "scores", "row_logsumexp", "softmax_rows",
     "attention_forward", "bwd_preprocess", "softmax_backward",
     "attention_backward", "topk_allowed", "sparse_forward", "sparse_backward",
+    "gqa_forward", "gqa_backward",
 ]
 
 
@@ -248,3 +249,40 @@ def sparse_backward(q, k, v, do, idx, topk_len, scale: float):
         np.add.at(dk, j, scale * (ds.T @ q[:, i, :]))
         np.add.at(dv, j, p.T @ do_i)
     return {"dq": dq, "dk": dk, "dv": dv, "D": D, "o": o, "lse": lse}
+
+
+# ----------------------------------------------------------------------------
+# Grouped-query attention: several query heads share one K/V head, as all the
+# query heads of the sparse variant share its single K/V head (cudnn-frontend
+# PR #684, DSA); the K/V gradients are then sums over the sharing heads.
+# ----------------------------------------------------------------------------
+def _expand_kv(x, h: int):
+    """[..., Hkv, N, d] -> [..., H, N, d]: query head c * (H / Hkv) + r uses
+    K/V head c."""
+    x = np.asarray(x, dtype=np.float64)
+    hkv = x.shape[-3]
+    if h % hkv != 0:
+        raise ValueError("Hkv must divide H")
+    return np.repeat(x, h // hkv, axis=-3)
+
+
+def gqa_forward(q, k, v, scale: float, causal: bool = False):
+    """q [..., H, N, d]; k, v [..., Hkv, N, d].  Dense attention per query head
+    with K/V head h / (H / Hkv).  Returns (O [..., H, N, dv], L [..., H, N])."""
+    h = np.asarray(q).shape[-3]
+    return attention_forward(q, _expand_kv(k, h), _expand_kv(v, h), scale, causal=causal)
+
+
+def gqa_backward(q, k, v, do, scale: float, causal: bool = False, o_for_D=None):
+    """Backward of ``gqa_forward``: per query head as ``attention_backward``,
+    then dK and dV of each K/V head summed over the query heads that read it.
+    Returns dict with dq [..., H, N, d], dk / dv [..., Hkv, N, d], D, o, lse."""
+    h = np.asarray(q).shape[-3]
+    hkv = np.asarray(k).shape[-3]
+    g = attention_backward(q, _expand_kv(k, h), _expand_kv(v, h), do, scale, causal=causal,
+                           o_for_D=o_for_D)
+    group = lambda x: x.reshape(x.shape[:-3] + (hkv, h // hkv) + x.shape[-2:]).sum(axis=-3)  # noqa: E731
+    g["dk"] = group(g["dk"])
+    g["dv"] = group(g["dv"])
+    return g
+

@@ -60,6 +60,40 @@ def test_backward_matches_finite_differences(causal, n, d):
         assert _rel(g[name], fd) < 1e-7, name
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_backward_matches_finite_differences(causal):
+    """Pins the head sums of dK / dV: 4 query heads on 2 K/V heads."""
+    rng = np.random.default_rng(99 + causal)
+    n, d = 5, 3
+    q, do = (_rand(rng, 1, 4, n, d) for _ in range(2))
+    k, v = (_rand(rng, 1, 2, n, d) for _ in range(2))
+    scale = 1.0 / math.sqrt(d)
+    g = oracle.gqa_backward(q, k, v, do, scale, causal=causal)
+    loss = lambda: float(np.sum(do * oracle.gqa_forward(q, k, v, scale, causal=causal)[0]))  # noqa: E731
+    for name, x in (("dq", q), ("dk", k), ("dv", v)):
+        assert g[name].shape == x.shape, name
+        assert _rel(g[name], _fd_grad(loss, x)) < 1e-7, name
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_mqa_equals_sparse_with_full_index_lists(causal):
+    """One K/V head for every query head is the sparse variant with every key
+    (or every key up to the row) in each row's list: two separately written
+    head-sum paths must agree."""
+    rng = np.random.default_rng(5 + causal)
+    h, n, d = 3, 6, 4
+    q, do = _rand(rng, h, n, d), _rand(rng, h, n, d)
+    k, v = _rand(rng, n, d), _rand(rng, n, d)
+    idx = np.tile(np.arange(n), (n, 1))
+    tl = np.arange(1, n + 1) if causal else None
+    sp = oracle.sparse_backward(q, k, v, do, idx, tl, 0.5)
+    gq = oracle.gqa_backward(q[None], k[None, None], v[None, None], do[None], 0.5, causal=causal)
+    for name in ("dq", "o", "lse", "D"):
+        np.testing.assert_allclose(gq[name][0], sp[name], rtol=1e-12, atol=1e-12, err_msg=name)
+    for name in ("dk", "dv"):
+        np.testing.assert_allclose(gq[name][0, 0], sp[name], rtol=1e-12, atol=1e-12, err_msg=name)
+
+
 def test_sparse_backward_matches_finite_differences():
     rng = np.random.default_rng(7)
     hq, nq, nkv, dqk, dv, topk = 2, 6, 6, 4, 3, 3
