@@ -319,6 +319,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="headline")
+    ap.add_argument("--hkv", type=int, default=None,
+                    help="grouped-query attention: K/V heads (dividing H); default H")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -350,11 +352,17 @@ def main(argv=None):
         return bench_sparse(args, SPARSE_CONFIGS[args.config])
     cfg = DENSE_CONFIGS[args.config]
     B, H, N, d = cfg.B, cfg.H, cfg.N, cfg.d
+    hkv = H if args.hkv is None else args.hkv
+    gqa = hkv != H
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print(f"[bench] {cfg.name}: B{B} H{H} N{N} d{d} causal={cfg.causal}", file=sys.stderr, flush=True)
 
-    inp = make_dense_inputs(cfg)
+    if gqa:
+        from attn_inputs import make_gqa_inputs
+        inp = make_gqa_inputs(cfg, hkv)
+    else:
+        inp = make_dense_inputs(cfg)
     import numpy as np
 
     def up(bits):
@@ -364,18 +372,20 @@ def main(argv=None):
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
     D = torch.empty((B, H, N), dtype=torch.float32, device=dev)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
-    ws = torch.empty((ea.attn_bwd_workspace_bytes(B, H, N, d),), dtype=torch.uint8, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty((ea.attn_bwd_gqa_workspace_bytes(B, H, hkv, N, d),), dtype=torch.uint8, device=dev)
+    fwd = ea.attn_fwd_gqa if gqa else ea.attn_fwd
+    bwd = ea.attn_bwd_gqa if gqa else ea.attn_bwd
     stream = torch.cuda.current_stream()
     ev = HipEvents()
 
-    ea.attn_fwd(q, k, v, cfg.causal, cfg.scale, o=o, lse=lse)
+    fwd(q, k, v, cfg.causal, cfg.scale, o=o, lse=lse)
     torch.cuda.synchronize()
 
     def step(events=None):
         ea.attn_bwd_preprocess(o, do, D=D)
-        ea.attn_bwd(q, k, v, do, lse, D, cfg.causal, cfg.scale, dq=dq, dk=dk, dv=dv,
-                    workspace=ws, main_events=events)
+        bwd(q, k, v, do, lse, D, cfg.causal, cfg.scale, dq=dq, dk=dk, dv=dv,
+            workspace=ws, main_events=events)
 
     for _ in range(args.warmup):
         step()
@@ -400,11 +410,11 @@ def main(argv=None):
 
     # forward, timed on its own (not part of the metric)
     for _ in range(max(2, args.warmup // 2)):
-        ea.attn_fwd(q, k, v, cfg.causal, cfg.scale, o=o, lse=lse)
+        fwd(q, k, v, cfg.causal, cfg.scale, o=o, lse=lse)
     torch.cuda.synchronize()
     ev.rt.hipEventRecord(ctypes.c_void_p(t0), ctypes.c_void_p(stream.cuda_stream))
     for _ in range(K):
-        ea.attn_fwd(q, k, v, cfg.causal, cfg.scale, o=o, lse=lse)
+        fwd(q, k, v, cfg.causal, cfg.scale, o=o, lse=lse)
     ev.rt.hipEventRecord(ctypes.c_void_p(t1), ctypes.c_void_p(stream.cuda_stream))
     torch.cuda.synchronize()
     fwd_ms = ev.elapsed_ms(t0, t1) / K
@@ -417,7 +427,8 @@ def main(argv=None):
     fl = bwd_flops(B, H, N, d, cfg.causal)
     value = tflops(fl, ms_step)
     main_tf = tflops(DKDV_FLOP_SHARE * fl, main_avg)
-    traffic = _traffic()
+    # the committed counter summary covers the headline workload only
+    traffic = _traffic() if (cfg.name == "headline" and not gqa) else None
     line = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -428,13 +439,16 @@ def main(argv=None):
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": round(value / PAGES_BWD_TFLOPS, 4) if cfg.name == "headline" else None,
+        "vs_baseline": round(value / PAGES_BWD_TFLOPS, 4) if (cfg.name == "headline" and not gqa) else None,
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
             "workload": f"{'causal' if cfg.causal else 'non-causal'} attention backward "
-                        f"(preprocess + fused backward) B{B} H{H} N{N} d{d} bf16, seed {cfg.seed}",
+                        f"(preprocess + fused backward) B{B} H{H}"
+                        + (f" Hkv{hkv} (grouped-query)" if gqa else "")
+                        + f" N{N} d{d} bf16, seed {cfg.seed}",
             "B": B, "H": H, "N": N, "d": d, "causal": cfg.causal, "scale": cfg.scale,
+            **({"Hkv": hkv} if gqa else {}),
         },
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 3),
         "peak_tflops": PEAK_BF16_TFLOPS,
@@ -455,7 +469,7 @@ def main(argv=None):
             "traffic": traffic,
         },
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not gqa:       # the oracle leg times the dense workload
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(inp, cfg, args.cpu_seconds)
     print(json.dumps(line), flush=True)

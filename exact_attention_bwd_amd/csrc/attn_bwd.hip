@@ -96,6 +96,27 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(float* __restrict__ Lb,
     }
 }
 
+// Grouped-query attention with the query heads of a group split over NS
+// workgroups: dK = sum of the NS fp32 partials (part), dV likewise (the block
+// after them), summed in part order and rounded to bf16.  n = B * Hkv * N * d
+// elements of each, a multiple of 4.
+__global__ __launch_bounds__(256) void gqa_reduce_kernel(const float* __restrict__ part,
+                                                         __bf16* __restrict__ dK,
+                                                         __bf16* __restrict__ dV, int NS, long long n) {
+    for (long long i = ((long long)blockIdx.x * 256 + threadIdx.x) * 4; i < 2 * n;
+         i += (long long)gridDim.x * 256 * 4) {
+        const bool isv = i >= n;
+        const long long e = isv ? i - n : i;
+        const float* src = part + (isv ? (long long)NS * n : 0) + e;
+        f32x4 acc = *reinterpret_cast<const f32x4*>(src);
+        for (int sp = 1; sp < NS; ++sp) acc += *reinterpret_cast<const f32x4*>(src + (long long)sp * n);
+        bf16x4 out;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) out[c] = (__bf16)acc[c];
+        *reinterpret_cast<bf16x4*>((isv ? dV : dK) + e) = out;
+    }
+}
+
 // ----------------------------------------------------------------------------
 // Fused backward main kernel
 // ----------------------------------------------------------------------------
@@ -174,7 +195,8 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                      const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                      const float* __restrict__ Lb, const float* __restrict__ Dp,
                      __bf16* __restrict__ dSw, __bf16* __restrict__ Kimg, __bf16* __restrict__ dK,
-                     __bf16* __restrict__ dV, int BH, int H, int G, int N, int n_pad, float scale) {
+                     __bf16* __restrict__ dV, int BH, int H, int G, int NS, float* __restrict__ part,
+                     int N, int n_pad, float scale) {
     using S = Smem<HD>;
     constexpr int KSD = HD / 16;                 // k steps over the head dim
     constexpr int DB = HD / 32;                  // 32-wide blocks of the head dim
@@ -194,14 +216,15 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const int tc = (N + BC - 1) / BC;
     const int tr_count = (N + BR - 1) / BR;
     const int logical = xcd_remap(blockIdx.x, BH * tc);
-    const int bh = logical / tc;                 // K / V head (BH = B * H / G of them)
     const int j = logical % tc;                  // heavy (small j) first when causal
     const int k0 = j * BC;
-
+    // grouped-query attention: BH = B * (H / G) * NS workgroup rows, one per
+    // (K / V head bh, part sp of its G query heads); the part's G / NS query
+    // heads hq0 .. are summed in registers, the NS parts in gqa_reduce_kernel
+    const int bh = (logical / tc) / NS, sp = (logical / tc) % NS;
+    const int GS = G / NS;
     const size_t head = (size_t)bh * N * HD;     // K, V, dK, dV
-    // grouped-query attention: the G query heads hq0 .. hq0 + G - 1 share this
-    // K / V head; their contributions to dK_j and dV_j are summed in registers
-    const int hq0 = (bh / (H / G)) * H + (bh % (H / G)) * G;
+    const int hq0 = (bh / (H / G)) * H + (bh % (H / G)) * G + sp * GS;
 
     __bf16* const QB = reinterpret_cast<__bf16*>(smem + S::off_q);   // Q buffers; dO at +2 tiles
     __bf16* const KB = reinterpret_cast<__bf16*>(smem + S::off_k);   // K; V at +BC*HD
@@ -263,7 +286,7 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     //      the waves; each block is two transposing reads of the K tile
     {
         constexpr int NBLK = DB * (BC / 16);
-        const __amdgpu_buffer_rsrc_t kr = make_rsrc(Kimg + kimg_tile(bh, j, tc, HD), BC * HD * 2);
+        const __amdgpu_buffer_rsrc_t kr = make_rsrc(Kimg + kimg_tile(bh, j, tc, HD), sp == 0 ? BC * HD * 2 : 0);
 #pragma unroll
         for (int b = 0; b < NBLK / NW; ++b) {
             const int blk = w * (NBLK / NW) + b;
@@ -287,10 +310,10 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const float sl2 = scale * kLog2e;
     const int key_lane = k0 + kw * 32 + l32;     // this lane's key (accumulator column)
 
-    for (int step = 0, buf = 0; step < G * nt; ++step, buf ^= 1) {
+    for (int step = 0, buf = 0; step < GS * nt; ++step, buf ^= 1) {
         const int gq = step / nt, it = it0 + step % nt;
         const int q0 = it * BR;
-        if (step + 1 < G * nt)                   // lands during this iteration
+        if (step + 1 < GS * nt)                  // lands during this iteration
             stage_tile((step + 1) / nt, it0 + (step + 1) % nt, buf ^ 1);
         const __bf16* Qs = QB + buf * TILE_EL;
         const __bf16* dOs = Qs + 2 * TILE_EL;
@@ -382,9 +405,17 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
             const float tot = (qh ? dk[db][r] : dv[db][r]) + other[(db * 16 + r) * 64 + lane];
             const int key = k0 + kw * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
             if (key < N) {
-                const size_t off = head + (size_t)key * HD + db * 32 + l32;
-                if (qh) dK[off] = (__bf16)(tot * scale);
-                else dV[off] = (__bf16)tot;
+                const size_t off = (size_t)key * HD + db * 32 + l32;
+                if (NS > 1) {
+                    // fp32 partial of part sp: dK block, then the dV block
+                    const size_t bkv = BH / NS, pb = ((size_t)sp * bkv + bh) * N * HD + off;
+                    if (qh) part[pb] = tot * scale;
+                    else part[(size_t)NS * bkv * N * HD + pb] = tot;
+                } else if (qh) {
+                    dK[head + off] = (__bf16)(tot * scale);
+                } else {
+                    dV[head + off] = (__bf16)tot;
+                }
             }
         }
     }
@@ -423,7 +454,8 @@ void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict_
                          const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                          const float* __restrict__ Lb, const float* __restrict__ Dp,
                          __bf16* __restrict__ dSw, __bf16* __restrict__ Kimg,
-                         __bf16* __restrict__ dK, __bf16* __restrict__ dV, int BH, int H, int G, int N,
+                         __bf16* __restrict__ dK, __bf16* __restrict__ dV, int BH, int H, int G, int NS,
+                         float* __restrict__ part, int N,
                          int n_pad, float scale) {
     constexpr int HD = 128;
     using S = Smem2;
@@ -468,10 +500,14 @@ void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict_
     const int k0 = j * BC2;
     const int kw0 = k0 + 64 * w;                 // this wave's first key
 
-    const size_t head = (size_t)bh * N * HD;     // K, V, dK, dV (BH = B * H / G heads)
-    // grouped-query attention: the G query heads hq0 .. hq0 + G - 1 share this
-    // K / V head; their contributions to dK_j and dV_j are summed in registers
-    const int hq0 = (bh / (H / G)) * H + (bh % (H / G)) * G;
+    // grouped-query attention: the mapped row is (K / V head, part sp of its
+    // G query heads); the part's G / NS query heads hq0 .. are summed in
+    // registers, the NS parts in gqa_reduce_kernel
+    const int sp = bh % NS;
+    bh /= NS;
+    const int GS = G / NS;
+    const size_t head = (size_t)bh * N * HD;     // K, V, dK, dV
+    const int hq0 = (bh / (H / G)) * H + (bh % (H / G)) * G + sp * GS;
     const __bf16* VS = reinterpret_cast<const __bf16*>(smem + S::off_v);
     const __bf16* KS = reinterpret_cast<const __bf16*>(smem + S::off_kstage);
 
@@ -507,7 +543,7 @@ void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict_
         // 128-key image tile jt = w >> 1 of this workgroup; 32 blocks of 1 KiB,
         // 16 per wave
         const int jt = w >> 1, jg = 2 * j + jt;
-        if (jg < tc) {
+        if (jg < tc && sp == 0) {
             const __amdgpu_buffer_rsrc_t kr = make_rsrc(Kimg + kimg_tile(bh, jg, tc, HD), BC * HD * 2);
 #pragma unroll
             for (int b = 0; b < 16; ++b) {
@@ -558,10 +594,10 @@ void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict_
     // block 1 at + 8 KiB
     const uint32_t aV = lds_addr(VS) + (uint32_t)((64 * w * HD + ob0) * 2);
 
-    for (int step = 0, buf = 0; step < G * nt; ++step, buf ^= 1) {
+    for (int step = 0, buf = 0; step < GS * nt; ++step, buf ^= 1) {
         const int gq = step / nt, it = tr_count - 1 - step % nt;
         const int q0 = it * BR;
-        if (step + 1 < G * nt)                   // lands during this iteration
+        if (step + 1 < GS * nt)                  // lands during this iteration
             stage_tile((step + 1) / nt, tr_count - 1 - (step + 1) % nt, buf ^ 1);
         const __bf16* Qs = reinterpret_cast<const __bf16*>(smem + S::off_q) + buf * TILE_EL;
         const __bf16* dOs = reinterpret_cast<const __bf16*>(smem + S::off_do) + buf * TILE_EL;
@@ -753,9 +789,16 @@ void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict_
             for (int r = 0; r < 16; ++r) {
                 const int key = kw0 + 32 * kb + (r >> 2) * 8 + g * 4 + (r & 3);
                 if (key < N) {
-                    const size_t off = head + (size_t)key * HD + db * 32 + l32;
-                    dV[off] = (__bf16)dv[kb][db][r];
-                    dK[off] = (__bf16)(dk[kb][db][r] * scale);
+                    const size_t off = (size_t)key * HD + db * 32 + l32;
+                    if (NS > 1) {
+                        // fp32 partial of part sp: dK block, then the dV block
+                        const size_t bkv = BH / NS, pb = ((size_t)sp * bkv + bh) * N * HD + off;
+                        part[pb] = dk[kb][db][r] * scale;
+                        part[(size_t)NS * bkv * N * HD + pb] = dv[kb][db][r];
+                    } else {
+                        dV[head + off] = (__bf16)dv[kb][db][r];
+                        dK[head + off] = (__bf16)(dk[kb][db][r] * scale);
+                    }
                 }
             }
 }
@@ -941,25 +984,50 @@ hipError_t launch_bwd_preprocess(const void* o, const void* dO, float* D, int BH
 }
 
 // Workspace: [Lb BH x n_pad fp32][D BH x n_pad fp32][dS tiles BH x T_r x T_c
-// x (BC x BR) bf16][K image BH / G x T_c x (BC x d) bf16] for BH query heads
+// x (BC x BR) bf16][K image BH / G x T_c x (BC x d) bf16][grouped-query
+// partials: 2 x NS x BH / G x N x d fp32, only when NS > 1] for BH query heads
 // and BH / G key / value heads.  Every dS tile the dQ kernel reads is written
 // by the dK/dV kernel first (causal: exactly the tiles with j <= i / 2), and so
-// is every K image tile.
+// is every K image tile and every partial.
 static size_t n_pad_of(int N) { return (size_t)((N + bwd::BR - 1) / bwd::BR) * bwd::BR; }
+
+// key tiles per K / V head of the dK/dV grid
+static int dkdv_tiles(int N, int d) {
+#ifndef ATTN_DKDV_W32
+    if (d == 128) return (N + bwd::BC2 - 1) / bwd::BC2;
+#endif
+    return (N + bwd::BC - 1) / bwd::BC;
+}
+
+// Parts the G query heads of a group are split over: 1 (all in one
+// workgroup, no partials) unless that leaves fewer than about six workgroups
+// per CU, in which case the smallest divisor of G that reaches that.
+static int gqa_parts(int BHkv, int N, int d, int G) {
+    const long long rows = (long long)BHkv * dkdv_tiles(N, d);
+    int ns = 1;
+    while (ns < G && rows * ns < 1536) {
+        int nx = ns + 1;
+        while (G % nx) ++nx;
+        ns = nx;
+    }
+    return ns;
+}
 
 size_t bwd_workspace_bytes(int BH, int G, int N, int d) {
     const size_t rows = (size_t)BH * n_pad_of(N);
     const size_t tr = (N + bwd::BR - 1) / bwd::BR, tc = (N + bwd::BC - 1) / bwd::BC;
+    const int ns = gqa_parts(BH / G, N, d, G);
+    const size_t parts = ns > 1 ? 2 * (size_t)ns * (BH / G) * N * d * sizeof(float) : 0;
     return 2 * rows * sizeof(float) + (size_t)BH * tr * tc * bwd::DST_EL * 2 +
-           (size_t)(BH / G) * tc * bwd::BC * d * 2;
+           (size_t)(BH / G) * tc * bwd::BC * d * 2 + parts;
 }
 
-// BHkv = B * H / G key / value heads (the dK/dV grid)
+// BHkv = B * H / G key / value heads (the dK/dV grid has BHkv * ns rows)
 template <int HD, bool CAUSAL>
 static hipError_t launch_dkdv(const void* q, const void* k, const void* v, const void* dO,
                               const float* Lb, const float* Dp, __bf16* dSw, __bf16* kimg, void* dk,
-                              void* dv, int BHkv, int H, int G, int N, int n_pad, float scale,
-                              hipStream_t stream) {
+                              void* dv, int BHkv, int H, int G, int ns, float* part, int N, int n_pad,
+                              float scale, hipStream_t stream) {
 #ifndef ATTN_DKDV_W32
     if (HD == 128) {
         using S2 = bwd::Smem2;
@@ -968,9 +1036,10 @@ static hipError_t launch_dkdv(const void* q, const void* k, const void* v, const
                                            hipFuncAttributeMaxDynamicSharedMemorySize, S2::bytes);
         if (e != hipSuccess) return e;
         const int tc2 = (N + bwd::BC2 - 1) / bwd::BC2;
-        hipLaunchKernelGGL(kern, dim3(BHkv * tc2), dim3(bwd::NW2 * 64), S2::bytes, stream,
+        hipLaunchKernelGGL(kern, dim3(BHkv * ns * tc2), dim3(bwd::NW2 * 64), S2::bytes, stream,
                            (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dO,
-                           Lb, Dp, dSw, kimg, (__bf16*)dk, (__bf16*)dv, BHkv, H, G, N, n_pad, scale);
+                           Lb, Dp, dSw, kimg, (__bf16*)dk, (__bf16*)dv, BHkv * ns, H, G, ns, part, N,
+                           n_pad, scale);
         return hipGetLastError();
     }
 #endif
@@ -980,9 +1049,9 @@ static hipError_t launch_dkdv(const void* q, const void* k, const void* v, const
                                        hipFuncAttributeMaxDynamicSharedMemorySize, S::bytes);
     if (e != hipSuccess) return e;
     const int tc = (N + bwd::BC - 1) / bwd::BC;
-    hipLaunchKernelGGL(kern, dim3(BHkv * tc), dim3(bwd::NT), S::bytes, stream, (const __bf16*)q,
+    hipLaunchKernelGGL(kern, dim3(BHkv * ns * tc), dim3(bwd::NT), S::bytes, stream, (const __bf16*)q,
                        (const __bf16*)k, (const __bf16*)v, (const __bf16*)dO, Lb, Dp, dSw, kimg,
-                       (__bf16*)dk, (__bf16*)dv, BHkv, H, G, N, n_pad, scale);
+                       (__bf16*)dk, (__bf16*)dv, BHkv * ns, H, G, ns, part, N, n_pad, scale);
     return hipGetLastError();
 }
 
@@ -997,14 +1066,22 @@ static hipError_t launch_dq(const __bf16* kimg, const __bf16* dSw, void* dq, int
 
 template <int HD, bool CAUSAL>
 static hipError_t launch_pair(const void* q, const void* k, const void* v, const void* dO,
-                              const float* Lb, const float* Dp, __bf16* dSw, __bf16* kimg, void* dq,
-                              void* dk, void* dv, int BH, int H, int G, int N, int n_pad, float scale,
-                              hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+                              const float* Lb, const float* Dp, __bf16* dSw, __bf16* kimg, float* part,
+                              void* dq, void* dk, void* dv, int BH, int H, int G, int N, int n_pad,
+                              float scale, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+    const int ns = gqa_parts(BH / G, N, HD, G);
     hipError_t e;
     if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
-    e = launch_dkdv<HD, CAUSAL>(q, k, v, dO, Lb, Dp, dSw, kimg, dk, dv, BH / G, H, G, N, n_pad, scale, stream);
+    e = launch_dkdv<HD, CAUSAL>(q, k, v, dO, Lb, Dp, dSw, kimg, dk, dv, BH / G, H, G, ns, part, N, n_pad,
+                                scale, stream);
     if (e != hipSuccess) return e;
     if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
+    if (ns > 1) {
+        const long long n = (long long)(BH / G) * N * HD;
+        hipLaunchKernelGGL(gqa_reduce_kernel, dim3(grid_for(2 * n, 1024, 16384)), dim3(256), 0, stream,
+                           part, (__bf16*)dk, (__bf16*)dv, ns, n);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     return launch_dq<HD, CAUSAL>(kimg, dSw, dq, BH, H, G, N, scale, stream);
 }
 
@@ -1020,15 +1097,16 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* d
     __bf16* dSw = (__bf16*)(Dp + rows);
     const size_t tr = (N + bwd::BR - 1) / bwd::BR, tc = (N + bwd::BC - 1) / bwd::BC;
     __bf16* kimg = dSw + (size_t)BH * tr * tc * bwd::DST_EL;
+    float* part = (float*)(kimg + (size_t)(BH / G) * tc * bwd::BC * d);
     hipLaunchKernelGGL(bwd_prep_kernel, dim3(grid_for((long long)rows, 256, 4096)), dim3(256), 0,
                        stream, Lb, Dp, lse, D, BH, N, n_pad);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (d == 128)
-        return causal ? launch_pair<128, true>(q, k, v, dO, Lb, Dp, dSw, kimg, dq, dk, dv, BH, H, G, N, n_pad, scale, stream, main_start, main_stop)
-                      : launch_pair<128, false>(q, k, v, dO, Lb, Dp, dSw, kimg, dq, dk, dv, BH, H, G, N, n_pad, scale, stream, main_start, main_stop);
-    return causal ? launch_pair<64, true>(q, k, v, dO, Lb, Dp, dSw, kimg, dq, dk, dv, BH, H, G, N, n_pad, scale, stream, main_start, main_stop)
-                  : launch_pair<64, false>(q, k, v, dO, Lb, Dp, dSw, kimg, dq, dk, dv, BH, H, G, N, n_pad, scale, stream, main_start, main_stop);
+        return causal ? launch_pair<128, true>(q, k, v, dO, Lb, Dp, dSw, kimg, part, dq, dk, dv, BH, H, G, N, n_pad, scale, stream, main_start, main_stop)
+                      : launch_pair<128, false>(q, k, v, dO, Lb, Dp, dSw, kimg, part, dq, dk, dv, BH, H, G, N, n_pad, scale, stream, main_start, main_stop);
+    return causal ? launch_pair<64, true>(q, k, v, dO, Lb, Dp, dSw, kimg, part, dq, dk, dv, BH, H, G, N, n_pad, scale, stream, main_start, main_stop)
+                  : launch_pair<64, false>(q, k, v, dO, Lb, Dp, dSw, kimg, part, dq, dk, dv, BH, H, G, N, n_pad, scale, stream, main_start, main_stop);
 }
 
 }  // namespace attn

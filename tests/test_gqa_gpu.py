@@ -51,27 +51,39 @@ def test_gqa_end_to_end(lib, cfg, hkv):
     assert_lse(from_dev(out["lse"]), ref["lse"])
 
 
-def test_gqa_full_length_group_sums(lib):
-    """B1 H16 Hkv2 N4096 d128 causal: the whole GPU path at full length; dK / dV
-    of K/V heads 0 and 1 (each the sum over 8 query heads) and dQ, O, L of the
-    first and last query head checked element by element."""
-    cfg = DenseConfig("gqa8_c128_4k", 1, 16, 4096, 128, True, seed=27)
-    hkv = 2
-    say(f"[parity-gqa-full] B1 H16 Hkv2 N4096 d128 causal")
+FULL = [
+    # one K/V head's 8 query heads split over 8 workgroups (fp32 partials)
+    (DenseConfig("gqa8_c128_4k", 1, 16, 4096, 128, True, seed=27), 2),
+    # 4 query heads per K/V head: two per workgroup at d = 128 (two partials),
+    # all four in one workgroup at d = 64 (no partials)
+    (DenseConfig("gqa4_c128_b8", 8, 32, 4096, 128, True, seed=28), 8),
+    (DenseConfig("gqa4_n64_b8", 8, 32, 4096, 64, False, seed=29), 8),
+]
+
+
+@pytest.mark.parametrize("cfg,hkv", FULL, ids=[c.name for c, _ in FULL])
+def test_gqa_full_length_group_sums(lib, cfg, hkv):
+    """The whole GPU path at full length; dK / dV of the first and last K/V
+    head (each the sum over its query heads) and dQ, O, L of the first and last
+    query head of those groups checked element by element."""
+    say(f"[parity-gqa-full] {cfg.name} B{cfg.B} H{cfg.H} Hkv{hkv} N{cfg.N} d{cfg.d} causal={cfg.causal}")
     inp = make_gqa_inputs(cfg, hkv)
     out = _run(lib, inp, cfg)
     import torch
     for n in ("o", "lse", "D", "dq", "dk", "dv"):
         assert not torch.isnan(out[n]).any().item(), f"{n} has NaN (unwritten sentinel)"
-    f = {n: bf16_bits_to_f64(inp[n]) for n in ("q", "k", "v", "do")}
     G = cfg.H // hkv
-    for c in range(hkv):
-        sl = slice(c * G, (c + 1) * G)
-        ref = oracle.gqa_backward(f["q"][:, sl], f["k"][:, c:c + 1], f["v"][:, c:c + 1], f["do"][:, sl],
-                                  cfg.scale, causal=True)
-        assert_close(f"dk[{c}]", from_dev(out["dk"])[:, c:c + 1], ref["dk"])
-        assert_close(f"dv[{c}]", from_dev(out["dv"])[:, c:c + 1], ref["dv"])
+    q4 = lambda n: inp[n].reshape(cfg.B * cfg.H, cfg.N, cfg.d)          # noqa: E731
+    k4 = lambda n: inp[n].reshape(cfg.B * hkv, cfg.N, cfg.d)            # noqa: E731
+    res = {n: from_dev(out[n]).reshape((-1,) + tuple(out[n].shape[2:])) for n in out}
+    for c in sorted({0, cfg.B * hkv - 1}):
+        hs = slice(c * G, (c + 1) * G)                                  # its query heads (flattened)
+        f = {"q": bf16_bits_to_f64(q4("q")[hs])[None], "do": bf16_bits_to_f64(q4("do")[hs])[None],
+             "k": bf16_bits_to_f64(k4("k")[c])[None, None], "v": bf16_bits_to_f64(k4("v")[c])[None, None]}
+        ref = oracle.gqa_backward(f["q"], f["k"], f["v"], f["do"], cfg.scale, causal=cfg.causal)
+        assert_close(f"dk[{c}]", res["dk"][c], ref["dk"][0, 0])
+        assert_close(f"dv[{c}]", res["dv"][c], ref["dv"][0, 0])
         for h in (0, G - 1):
             for n in ("o", "D", "dq"):
-                assert_close(f"{n}[{c * G + h}]", from_dev(out[n])[:, c * G + h], ref[n][:, h])
-            assert_lse(from_dev(out["lse"])[:, c * G + h], ref["lse"][:, h])
+                assert_close(f"{n}[{c * G + h}]", res[n][c * G + h], ref[n][0, h])
+            assert_lse(res["lse"][c * G + h], ref["lse"][0, h])
