@@ -774,17 +774,16 @@ void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict_
         __syncthreads();                         // next tile landed; this one free
     }
 
-    // ---- epilogue: dV, dK (scaled) of this wave's 64 keys, once the last
-    //      accumulations have left the matrix core
-    asm volatile("s_nop 15\n\ts_nop 15"
-                 : "+a"(dv[0][0]), "+a"(dv[0][1]), "+a"(dv[0][2]), "+a"(dv[0][3]),
-                   "+a"(dv[1][0]), "+a"(dv[1][1]), "+a"(dv[1][2]), "+a"(dv[1][3]),
-                   "+a"(dk[0][0]), "+a"(dk[0][1]), "+a"(dk[0][2]), "+a"(dk[0][3]),
-                   "+a"(dk[1][0]), "+a"(dk[1][1]), "+a"(dk[1][2]), "+a"(dk[1][3]));
+    // ---- epilogue: dV, dK (scaled) of this wave's 64 keys, each pair of
+    //      tiles once its last accumulations have left the matrix core.  One
+    //      settle per pair: a single settle over all sixteen makes the
+    //      compiler regroup the registers first, and its moves would read
+    //      the last product's tile before that product has landed.
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DB; ++db) {
+            asm volatile("s_nop 15\n\ts_nop 7" : "+a"(dv[kb][db]), "+a"(dk[kb][db]));
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int key = kw0 + 32 * kb + (r >> 2) * 8 + g * 4 + (r & 3);
@@ -801,6 +800,7 @@ void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict_
                     }
                 }
             }
+        }
 }
 
 // ----------------------------------------------------------------------------

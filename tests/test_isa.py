@@ -2,15 +2,23 @@
 the dQ kernel and the d = 128 forward kernel (CPU only: hipcc cross-compiles
 gfx950 without a GPU).
 
-These kernels issue LDS and global loads from inline assembly and wait for them
-with explicit s_waitcnt counts, so the compiler does not know when a load's
-destination registers are written.  A register copy that the compiler places
-between such a load and its wait would read stale data.  The kernels are
-written so that the compiler never needs to copy a vector register; this test
-keeps it that way across source and compiler changes by requiring every
-compiler-generated v_mov in them to take an immediate or a scalar source
-(copies written inside the kernels' own assembly blocks are deliberate and
-exempt), and by requiring that they spill nothing.
+These kernels issue LDS and global loads and matrix-core products from inline
+assembly and wait for them with explicit s_waitcnt counts and s_nop settles,
+so the compiler knows neither when a load's destination registers are written
+nor when a product's result lands.  A register copy that the compiler places
+between such an instruction and its wait or settle would read stale data.
+The kernels are written so that no such copy is needed; this test keeps it
+that way across source and compiler changes:
+
+- every compiler-generated v_mov takes an immediate, a scalar, or a register
+  that holds only an immediate (a zero fill) as its source;
+- no compiler move reads an AGPR that the kernel's assembly writes while
+  products are still being issued;
+- after the last product, no compiler move reads that product's result
+  before the settle that follows it;
+- and the kernels spill nothing.
+
+Copies inside the kernels' own assembly blocks are deliberate and exempt.
 """
 import os
 import re
@@ -57,7 +65,7 @@ def _body(lines, prefix):
     return lines[start:end]
 
 
-VMOV = re.compile(r"^\s*(v_mov_b32|v_mov_b64|v_pk_mov_b32)\S*\s+(\S+),\s*(.+)$")
+VMOV = re.compile(r"^\s*(v_mov_b32|v_mov_b64|v_pk_mov_b32|v_accvgpr_mov_b32|v_accvgpr_read_b32|v_accvgpr_write_b32)\S*\s+(\S+),\s*(.+)$")
 
 
 def _compiler_lines(body):
@@ -72,15 +80,78 @@ def _compiler_lines(body):
             yield l
 
 
+REG = re.compile(r"([va])\[?(\d+)(?::(\d+))?\]?$")
+
+
+def _regs(op):
+    """Registers named by an operand ('v5', 'a[16:19]'), as {('a', 16), ...}."""
+    m = REG.match(op.strip())
+    if not m:
+        return set()
+    lo = int(m.group(2))
+    return {(m.group(1), r) for r in range(lo, int(m.group(3) or lo) + 1)}
+
+
+STORE = re.compile(r"^\s*(ds_write|buffer_store|global_store|flat_store|scratch_store|s_)")
+IMM = re.compile(r"^-?(0x[0-9a-f]+|\d+(\.\d+)?)$")
+
+
 @pytest.mark.parametrize("src,kernel", KERNELS, ids=[k for _, k in KERNELS])
 def test_no_vector_register_copies(isa, src, kernel):
     body = _body(isa[src], kernel)
     assert any("v_mfma" in l for l in body), "kernel body not found"
+    mfma = [i for i, l in enumerate(body) if "v_mfma" in l]
+    first, last = mfma[0], mfma[-1]
+    settle = next((i for i in range(last, len(body)) if "s_nop 15" in body[i]), len(body))
+    # registers the kernels' own assembly writes (loads, products): the
+    # compiler knows neither when they land nor the products' latency
+    asm_dst, inside, asm_lines = set(), False, set()
+    for i, l in enumerate(body):
+        if "ASMSTART" in l:
+            inside = True
+        elif "ASMEND" in l:
+            inside = False
+        elif inside and l.strip() and not STORE.match(l):
+            asm_lines.add(i)
+            parts = l.split(None, 1)
+            if len(parts) > 1:
+                asm_dst |= _regs(parts[1].split(",")[0])
+    last_dst = _regs(body[last].split()[1].rstrip(",")) if last in asm_lines else set()
     bad = []
-    for l in _compiler_lines(body):
-        m = VMOV.match(l)
-        if m and re.match(r"v\[?\d", m.group(3).split(",")[0].strip()):
-            bad.append(l.strip())
+    inside = False
+    const = set()          # registers whose latest value is an immediate (zero fills)
+    for i, l in enumerate(body):
+        if "ASMSTART" in l:
+            inside = True
+            continue
+        if "ASMEND" in l:
+            inside = False
+            continue
+        if re.match(r"^\.LBB\S*:", l):
+            const = set()                        # a block may be reached from elsewhere
+            continue
+        parts = l.split(None, 1)
+        dst = _regs(parts[1].split(",")[0]) if len(parts) > 1 and not STORE.match(l) else set()
+        m = None if inside else VMOV.match(l)
+        if m is None:
+            const -= dst
+            continue
+        src_op = m.group(3).split(",")[0].strip()
+        srcs = _regs(src_op)
+        if IMM.match(src_op) or (srcs and srcs <= const):
+            const |= dst                         # an immediate, or a copy of one
+            continue
+        const -= dst
+        if not srcs:
+            continue                             # scalar source
+        from_v = any(k == "v" for k, _ in srcs)
+        if m.group(1).startswith("v_mov") or m.group(1) == "v_pk_mov_b32":
+            if from_v:
+                bad.append(l.strip())            # any copy of a VGPR
+        elif first <= i < last and srcs & asm_dst:
+            bad.append(l.strip())                # AGPR traffic among the products
+        elif last <= i < settle and srcs & last_dst:
+            bad.append(l.strip())                # the last product read before its settle
     assert not bad, f"{kernel}: vector register copies {bad[:5]}"
 
 
