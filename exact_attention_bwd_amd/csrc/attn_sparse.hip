@@ -649,20 +649,29 @@ __global__ __launch_bounds__(256) void sidx_fill_kernel(const int* __restrict__ 
 }
 
 // Per key: dV_j = sum over its (row, slot) pairs and head groups of the stored
-// contributions, dK_j = scale * the same sum of the dK parts; one wave per key,
-// in the fixed list order.  Lane l sums the 16-byte chunks l, l + 64, l + 128,
+// contributions, dK_j = scale * the same sum of the dK parts.  One workgroup
+// of RW waves per key: the key's list (in its fixed order) is cut into RW
+// contiguous segments, wave w sums segment w in list order, and the segment
+// sums are added in segment order, so that the result does not depend on
+// timing.  (A key can collect thousands of rows, the first keys of a causal
+// selection most of all; one wave per key left those few keys to set the
+// kernel's length.)  Lane l sums the 16-byte chunks l, l + 64, l + 128,
 // l + 192 of each 4352-byte contribution row and word 1024 + l; rows are
 // loaded four at a time so that 20 loads per lane are in flight.
-__global__ __launch_bounds__(256) void sbwd_reduce_kernel(const float* __restrict__ part,
-                                                          const int* __restrict__ off,
-                                                          const int* __restrict__ list,
-                                                          __bf16* __restrict__ dK,
-                                                          __bf16* __restrict__ dV, int Nkv, int G,
-                                                          int topk, float scale) {
+constexpr int RW = 4;                            // waves per key
+
+__global__ __launch_bounds__(RW * 64) void sbwd_reduce_kernel(const float* __restrict__ part,
+                                                             const int* __restrict__ off,
+                                                             const int* __restrict__ list,
+                                                             __bf16* __restrict__ dK,
+                                                             __bf16* __restrict__ dV, int Nkv, int G,
+                                                             int topk, float scale) {
     static_assert(PW == 4 * 256 + 64, "row layout: four 1 KiB chunks per 64 lanes and 64 words");
+    __shared__ f32x4 red4[RW - 1][4][64];
+    __shared__ float redt[RW - 1][64];
     const int lane = threadIdx.x & 63;
-    const int j = blockIdx.x * 4 + wave_id();
-    if (j >= Nkv) return;
+    const int w = wave_id();
+    const int j = blockIdx.x;
     f32x4 acc[4];
     float acct = 0.f;
 #pragma unroll
@@ -675,8 +684,10 @@ __global__ __launch_bounds__(256) void sbwd_reduce_kernel(const float* __restric
         const int i = pr / topk, s = pr - i * topk;
         return part + (((size_t)i * G + r % G) * topk + s) * PW;
     };
-    int r = 0;
-    for (; r + 4 <= nrows; r += 4) {
+    // this wave's segment [r0, r1)
+    const int r0 = (int)((long long)nrows * w / RW), r1 = (int)((long long)nrows * (w + 1) / RW);
+    int r = r0;
+    for (; r + 4 <= r1; r += 4) {
         f32x4 v[4][4];
         float t[4];
 #pragma unroll
@@ -693,11 +704,25 @@ __global__ __launch_bounds__(256) void sbwd_reduce_kernel(const float* __restric
             acct += t[u];
         }
     }
-    for (; r < nrows; ++r) {
+    for (; r < r1; ++r) {
         const float* row = row_of(r);
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc[c] += reinterpret_cast<const f32x4*>(row)[c * 64 + lane];
         acct += row[1024 + lane];
+    }
+    // segment sums 1 .. RW-1 to wave 0, added in segment order
+    if (w > 0) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) red4[w - 1][c][lane] = acc[c];
+        redt[w - 1][lane] = acct;
+    }
+    __syncthreads();
+    if (w != 0) return;
+#pragma unroll
+    for (int q = 0; q < RW - 1; ++q) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c] += red4[q][c][lane];
+        acct += redt[q][lane];
     }
     // columns 4 lane + 256 c (+0..3): c = 0, 1 are dV, c = 2, 3 and 1024 + lane are dK
 #pragma unroll
@@ -808,7 +833,7 @@ hipError_t launch_sparse_bwd(const void* q, const void* k, const void* v, const 
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (Nkv > 0) {
-        hipLaunchKernelGGL(sp::sbwd_reduce_kernel, dim3((Nkv + 3) / 4), dim3(256), 0, stream, part,
+        hipLaunchKernelGGL(sp::sbwd_reduce_kernel, dim3(Nkv), dim3(sp::RW * 64), 0, stream, part,
                            off, list, (__bf16*)dk, (__bf16*)dv, Nkv, G, topk, scale);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
