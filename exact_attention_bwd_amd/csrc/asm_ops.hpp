@@ -39,6 +39,11 @@ __device__ __forceinline__ void mfma_v0(f32x16& c, const bf16x8& a, const bf16x8
     asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(c) : "v"(a), "v"(b));
 }
 
+// c = a b + cin (cin another register tuple, not overwritten)
+__device__ __forceinline__ void mfma_vc(f32x16& c, const bf16x8& a, const bf16x8& b, const f32x16& cin) {
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(c) : "v"(a), "v"(b), "v"(cin));
+}
+
 __device__ __forceinline__ void mfma_v_settle2(f32x16& a, f32x16& b) {
     asm volatile("s_nop 15" : "+v"(a), "+v"(b));
 }

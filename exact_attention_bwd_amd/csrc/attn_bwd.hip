@@ -92,7 +92,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(float* __restrict__ Lb,
         const int n = (int)(i % n_pad);
         const bool in = n < N;
         Lb[i] = in ? lse[bh * N + n] * kLog2e : __builtin_inff();
-        Dp[i] = in ? D[bh * N + n] : 0.f;
+        Dp[i] = in ? -D[bh * N + n] : 0.f;       // -D: added to dP in the kernels
     }
 }
 
@@ -352,7 +352,7 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                 const int r = rr * 4 + e;
                 const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -lv[e]));
                 s[r] = p;
-                dp[r] = p * (dp[r] - dd[e]);
+                dp[r] = p * (dp[r] + dd[e]);      // dd holds -D
             }
         }
         // ---- P^T, dS^T as A operands (k = query, relabelled per lane group)
@@ -600,9 +600,7 @@ void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict_
         if (step + 1 < GS * nt)                  // lands during this iteration
             stage_tile((step + 1) / nt, tr_count - 1 - (step + 1) % nt, buf ^ 1);
         const __bf16* Qs = reinterpret_cast<const __bf16*>(smem + S::off_q) + buf * TILE_EL;
-        const __bf16* dOs = reinterpret_cast<const __bf16*>(smem + S::off_do) + buf * TILE_EL;
         const float* Ls = reinterpret_cast<const float*>(smem + S::off_l) + buf * BR;
-        const float* Ds = reinterpret_cast<const float*>(smem + S::off_d) + buf * BR;
         // dS stores go nowhere (buffer records 0) for a 128-key half past N
         const __amdgpu_buffer_rsrc_t dsr =
             make_rsrc(dSw + dst_tile(hq0 + gq, it, min(jst, tc - 1), tr_count, tc), jst < tc ? DST_EL * 2 : 0);
@@ -621,8 +619,9 @@ void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict_
         const uint32_t aQ = lds_addr(Qs) + (uint32_t)(ob0 * 2);
         const uint32_t aL = lds_addr(Ls) + (uint32_t)(g * 16);
 
-        // L of row group 0 of half h and its Q operands for S, loaded ahead
-        f32x4 lv[4];
+        // L of row group 0 of half h, its Q operands for S and its -D (the
+        // initial value of the dP accumulators), loaded ahead
+        f32x4 lv[4], dd[4];
         bf16x8 aq[KSD];
         auto load_s = [&](auto hI) {
             constexpr int h = decltype(hI)::value;
@@ -631,6 +630,10 @@ void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict_
                 constexpr int ks = decltype(ksI)::value;
                 lds_ld<h * 8192>(aq[ks], vxor<ks * 32>(aQ));
             });
+            static_for<0, 4>([&](auto rrI) {
+                constexpr int rr = decltype(rrI)::value;
+                lds_ld<512 + h * 128 + rr * 32>(dd[rr], aL);
+            });
         };
         load_s(std::integral_constant<int, 0>{});
         static_for<0, 2>([&](auto qbI) {
@@ -638,14 +641,14 @@ void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict_
             using SC = W64Sched;
             // A half runs four phases of 16 MFMAs: S, dP, dV, dK.  The
             // softmax VALU work is spread over the dP phase (P and its bf16
-            // packing) and the dV phase (dS = P o (dP - D) and its packing),
+            // packing) and the dV phase (dS = P o (dP - D) and its packing;
+            // the dP accumulators start from -D, so that is one product),
             // one share after each MFMA, so that it issues while the matrix
             // core works on the previous product; each slot ends in a
             // sched_barrier that keeps the compiler from regrouping it.
             // Elements are taken in the order (row group rr, key block kb).
             // Every LDS read is issued from assembly at a fixed point of
             // this schedule and waited for with the count W64Sched derives.
-            f32x4 dd[4];
             bf16x8 ado[KSD], bv[KSD][2];
             auto load_dp = [&](auto ksI) {
                 constexpr int ks = decltype(ksI)::value;
@@ -653,10 +656,6 @@ void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict_
                 const uint32_t av = vxor<ks * 32>(aV);
                 lds_ld<0>(bv[ks][0], av);
                 lds_ld<8192>(bv[ks][1], av);
-            };
-            auto load_dd = [&](auto rrI) {
-                constexpr int rr = decltype(rrI)::value;
-                lds_ld<512 + qb * 128 + rr * 32>(dd[rr], aL);
             };
             // step t = 4 k4 + db of the dV (src dO) or dK (src Q) phase
             u32x2 tb[8][2];
@@ -707,16 +706,30 @@ void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict_
                 if constexpr (m == 14) tr_step(std::integral_constant<int, 1>{}, IsDo{});
                 if constexpr (SC::P_DP(m) > 0) load_dp(std::integral_constant<int, ks + SC::PD>{});
                 if constexpr (SC::P_LV(m) > 0) lds_ld<qb * 128 + (rr + 1) * 32>(lv[rr + 1], aL);
-                if constexpr (SC::P_DD(m) > 0) load_dd(std::integral_constant<int, ((m - 9) >> 1)>{});
                 // each register is tied to the first wait that covers it only
-                if constexpr (kb == 1)
+                // (-D came with the half's first reads, before dO step 0)
+                if constexpr (m == 0)
+                    asm volatile("s_waitcnt lgkmcnt(%[n])"
+                                 : "+v"(ado[0]), "+v"(bv[0][0]), "+v"(lv[0]), "+v"(dd[0]), "+v"(dd[1]),
+                                   "+v"(dd[2]), "+v"(dd[3])
+                                 : [n] "n"(SC::wait_P(0) > 15 ? 15 : SC::wait_P(0)));
+                else if constexpr (kb == 1)
                     lgkm_wait<SC::wait_P(m)>(bv[ks][1]);
                 else if constexpr ((m & 3) == 0)
                     lgkm_wait<SC::wait_P(m)>(ado[ks], bv[ks][0], lv[rr]);
                 else
                     lgkm_wait<SC::wait_P(m)>(ado[ks], bv[ks][0]);
-                if constexpr (ks == 0) mfma_v0(dp[kb], ado[ks], bv[ks][kb]);
-                else mfma_v(dp[kb], ado[ks], bv[ks][kb]);
+                if constexpr (ks == 0) {
+                    // dP starts from -D: row m of the C layout holds D of
+                    // query row 8 (r / 4) + 4 g + r % 4, which dd[r / 4]
+                    // holds in its element r % 4
+                    f32x16 dinit;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) dinit[r] = dd[r >> 2][r & 3];
+                    mfma_vc(dp[kb], ado[0], bv[0][kb], dinit);
+                } else {
+                    mfma_v(dp[kb], ado[ks], bv[ks][kb]);
+                }
                 constexpr int ekb = (m >> 1) & 1;
 #pragma unroll
                 for (int x = 0; x < 2; ++x) {
@@ -731,24 +744,20 @@ void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict_
             // ---- dV += P^T dO; VALU slots: dS = P o (dP - D)
             static_for<0, 16>([&](auto mI) {
                 constexpr int m = decltype(mI)::value, t = m >> 1, kb = m & 1, rr = m >> 2;
-                if constexpr (SC::V_DD(m) > 0) load_dd(std::integral_constant<int, rr + 2>{});
                 if constexpr (kb == 0) {
                     // two steps of reads stay in flight: this phase's, then
                     // the first two of the dK phase
                     if constexpr (t + 2 < 8) tr_step(std::integral_constant<int, t + 2>{}, IsDo{});
                     else tr_step(std::integral_constant<int, t - 6>{}, IsQ{});
                 }
-                if constexpr ((m & 3) == 0)
-                    lgkm_wait<SC::wait_V(m)>(tb[t][0], tb[t][1], dd[rr]);
-                else if constexpr (kb == 0)
-                    lgkm_wait<SC::wait_V(m)>(tb[t][0], tb[t][1]);
+                if constexpr (kb == 0) lgkm_wait<SC::wait_V(m)>(tb[t][0], tb[t][1]);
                 if constexpr (m == 0 || m == 1) pa[m][1] = pack_c8(s[m], 8);
                 mfma_a(dv[kb][t & 3], pa[kb][t >> 2], cat_u(tb[t][0], tb[t][1]));
                 constexpr int ekb = (m >> 1) & 1;
 #pragma unroll
                 for (int x = 0; x < 2; ++x) {
                     const int r = 4 * rr + 2 * (m & 1) + x;
-                    dp[ekb][r] = s[ekb][r] * (dp[ekb][r] - dd[rr][r & 3]);
+                    dp[ekb][r] = s[ekb][r] * dp[ekb][r];     // dP already holds dP - D
                 }
                 if constexpr (m == 8 || m == 9) da[m - 8][0] = pack_c8(dp[m - 8], 0);
                 __builtin_amdgcn_sched_barrier(0);

@@ -8,14 +8,15 @@ compiles the header with the host compiler, prints the counts, and compares
 them with a slot-by-slot simulation of the kernel's issue order written out
 here independently:
 
-  * a half starts with L group 0 and the 8 Q operands of S in flight;
+  * a half starts with L group 0, the 8 Q operands of S and the 4 row groups
+    of -D (the dP accumulators' initial value) in flight;
   * S slot ks: wait for Q step ks, then (ks >= 8 - PD) read the dP operands
     of step ks - (8 - PD): dO, V block 0, V block 1;
   * dP slot m: transposed dO of dV step 0 / 1 (m = 12 / 14), the dP operands
-    of step m / 2 + PD (even m), L group m / 4 + 1 (m = 0, 4, 8), D group
-    0 / 1 (m = 9 / 11), then the wait for this slot's operands;
-  * dV slot m: D group m / 4 + 2 (m = 0, 4), then (even m) the transposed
-    reads of dV step m / 2 + 2, or of dK step m / 2 - 6 once those run out;
+    of step m / 2 + PD (even m), L group m / 4 + 1 (m = 0, 4, 8), then the
+    wait for this slot's operands (slot 0 also for -D);
+  * dV slot m: (even m) the transposed reads of dV step m / 2 + 2, or of dK
+    step m / 2 - 6 once those run out;
   * dK slot m: (even m, m < 12) transposed Q of dK step m / 2 + 2.
 """
 import os
@@ -65,7 +66,7 @@ def waits(tmp_path_factory):
 
 
 def simulate(pd):
-    seq = ["lv0"] + [f"aq{k}" for k in range(8)]
+    seq = ["lv0"] + [f"aq{k}" for k in range(8)] + [f"dd{r}" for r in range(4)]
     need = {}
 
     def wait(tag, names):
@@ -88,26 +89,22 @@ def simulate(pd):
             load_dp(ks + pd)
         if m % 4 == 0 and m < 12:
             seq.append(f"lv{rr + 1}")
-        if m in (9, 11):
-            seq.append(f"dd{(m - 9) // 2}")
-        if kb == 1:
+        if m == 0:
+            wait(("P", m), ["ado0", "bv0_0", "lv0", "dd0", "dd1", "dd2", "dd3"])
+        elif kb == 1:
             wait(("P", m), [f"bv{ks}_1"])
         elif m % 4 == 0:
             wait(("P", m), [f"ado{ks}", f"bv{ks}_0", f"lv{rr}"])
         else:
             wait(("P", m), [f"ado{ks}", f"bv{ks}_0"])
     for m in range(16):
-        t, kb, rr = m >> 1, m & 1, m >> 2
-        if m in (0, 4):
-            seq.append(f"dd{rr + 2}")
+        t, kb = m >> 1, m & 1
         if kb == 0:
             if t + 2 < 8:
                 seq.extend([f"trv{t + 2}a", f"trv{t + 2}b"])
             else:
                 seq.extend([f"trk{t - 6}a", f"trk{t - 6}b"])
-        if m % 4 == 0:
-            wait(("V", m), [f"trv{t}a", f"trv{t}b", f"dd{rr}"])
-        elif kb == 0:
+        if kb == 0:
             wait(("V", m), [f"trv{t}a", f"trv{t}b"])
         else:
             need[("V", m)] = -1
@@ -126,7 +123,7 @@ def test_waits_match_issue_order(waits):
     pd, got = waits
     assert 1 <= pd <= 8
     need, seq = simulate(pd)
-    # L 0, Q x 8, dP operands 8 x 3, L 1..3, D 0..3, transposed pairs 16 x 2
+    # L 0, Q x 8, -D 0..3, dP operands 8 x 3, L 1..3, transposed pairs 16 x 2
     assert len(seq) == 9 + 8 * 3 + 3 + 4 + 16 * 2, "every LDS read of a half issued exactly once"
     assert len(set(seq)) == len(seq)
     bad = {k: (got[k], v) for k, v in need.items() if got[k] != v}
