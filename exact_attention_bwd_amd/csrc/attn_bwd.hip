@@ -593,6 +593,11 @@ void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict_
     // row reads of V_j: this wave's rows, k step ks at ^ 32 ks bytes, key
     // block 1 at + 8 KiB
     const uint32_t aV = lds_addr(VS) + (uint32_t)((64 * w * HD + ob0) * 2);
+    uint32_t aVx[KSD];
+    static_for<0, KSD>([&](auto ksI) {
+        constexpr int ks = decltype(ksI)::value;
+        aVx[ks] = vxor<ks * 32>(aV);
+    });
 
     for (int step = 0, buf = 0; step < GS * nt; ++step, buf ^= 1) {
         const int gq = step / nt, it = tr_count - 1 - step % nt;
@@ -618,6 +623,13 @@ void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict_
         // + 512 bytes)
         const uint32_t aQ = lds_addr(Qs) + (uint32_t)(ob0 * 2);
         const uint32_t aL = lds_addr(Ls) + (uint32_t)(g * 16);
+        // the k-step addresses of the row reads, once per tile (the swizzle
+        // is an XOR, which no immediate offset can express)
+        uint32_t aQx[KSD];
+        static_for<0, KSD>([&](auto ksI) {
+            constexpr int ks = decltype(ksI)::value;
+            aQx[ks] = vxor<ks * 32>(aQ);
+        });
 
         // L of row group 0 of half h, its Q operands for S and its -D (the
         // initial value of the dP accumulators), loaded ahead
@@ -628,7 +640,7 @@ void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict_
             lds_ld<h * 128>(lv[0], aL);
             static_for<0, KSD>([&](auto ksI) {
                 constexpr int ks = decltype(ksI)::value;
-                lds_ld<h * 8192>(aq[ks], vxor<ks * 32>(aQ));
+                lds_ld<h * 8192>(aq[ks], aQx[ks]);
             });
             static_for<0, 4>([&](auto rrI) {
                 constexpr int rr = decltype(rrI)::value;
@@ -652,10 +664,9 @@ void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict_
             bf16x8 ado[KSD], bv[KSD][2];
             auto load_dp = [&](auto ksI) {
                 constexpr int ks = decltype(ksI)::value;
-                lds_ld<2 * S::TILE + qb * 8192>(ado[ks], vxor<ks * 32>(aQ));
-                const uint32_t av = vxor<ks * 32>(aV);
-                lds_ld<0>(bv[ks][0], av);
-                lds_ld<8192>(bv[ks][1], av);
+                lds_ld<2 * S::TILE + qb * 8192>(ado[ks], aQx[ks]);
+                lds_ld<0>(bv[ks][0], aVx[ks]);
+                lds_ld<8192>(bv[ks][1], aVx[ks]);
             };
             // step t = 4 k4 + db of the dV (src dO) or dK (src Q) phase
             u32x2 tb[8][2];
