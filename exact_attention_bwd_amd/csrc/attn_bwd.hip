@@ -782,8 +782,10 @@ void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict_
                 if constexpr (m >= 2 && m < 6) {
                     // run (sk, k4) = (0, 0) (1, 0) (0, 1) (1, 1) of this wave's block
                     constexpr int sk = m & 1, k4 = (m - 2) >> 1;
+                    // non-temporal: this kernel never reads dS back, and
+                    // the tiles should not push the shared Q / dO out of L2
                     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, da[sk][k4]), dsr,
-                                                           dst_run(qb, w & 1, sk, k4) + lane * 16, 0, 0);
+                                                           dst_run(qb, w & 1, sk, k4) + lane * 16, 0, 2);
                 }
                 mfma_a(dk[kb][t & 3], da[kb][t >> 2], cat_u(tb[t][0], tb[t][1]));
                 // the next half's L and Q operands, after the last wait
