@@ -801,28 +801,54 @@ void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict_
     //      settle per pair: a single settle over all sixteen makes the
     //      compiler regroup the registers first, and its moves would read
     //      the last product's tile before that product has landed.
+    //      Element r of tile (kb, db) is key 32 kb + 8 (r / 4) + 4 g + r % 4
+    //      of the wave, column 32 db + l32.
+    if (NS > 1) {
+        // fp32 partials of part sp: the dK block, then the dV block
+        const size_t bkv = BH / NS, pb0 = ((size_t)sp * bkv + bh) * N * HD;
+        const size_t pv = (size_t)NS * bkv * N * HD;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            asm volatile("s_nop 15\n\ts_nop 7" : "+a"(dv[kb][db]), "+a"(dk[kb][db]));
+            for (int db = 0; db < DB; ++db) {
+                asm volatile("s_nop 15\n\ts_nop 7" : "+a"(dv[kb][db]), "+a"(dk[kb][db]));
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = kw0 + 32 * kb + (r >> 2) * 8 + g * 4 + (r & 3);
-                if (key < N) {
-                    const size_t off = (size_t)key * HD + db * 32 + l32;
-                    if (NS > 1) {
-                        // fp32 partial of part sp: dK block, then the dV block
-                        const size_t bkv = BH / NS, pb = ((size_t)sp * bkv + bh) * N * HD + off;
+                for (int r = 0; r < 16; ++r) {
+                    const int key = kw0 + 32 * kb + (r >> 2) * 8 + g * 4 + (r & 3);
+                    if (key < N) {
+                        const size_t pb = pb0 + (size_t)key * HD + db * 32 + l32;
                         part[pb] = dk[kb][db][r] * scale;
-                        part[(size_t)NS * bkv * N * HD + pb] = dv[kb][db][r];
-                    } else {
-                        dV[head + off] = (__bf16)dv[kb][db][r];
-                        dK[head + off] = (__bf16)(dk[kb][db][r] * scale);
+                        part[pv + pb] = dv[kb][db][r];
                     }
                 }
             }
-        }
+    } else {
+        // bf16 through buffer resources over this wave's valid keys (keys at
+        // or past N fall outside them and are dropped): a lane offset, the
+        // key block 32 kb + 8 (r / 4) as the scalar offset, the rest immediate
+        // (readfirstlane: the values are wave-uniform, and a resource the
+        // compiler keeps in VGPRs turns every store into a waterfall loop)
+        const int kwu = __builtin_amdgcn_readfirstlane(kw0);
+        const int nkb = __builtin_amdgcn_readfirstlane(max(0, min(64, N - kwu)) * HD * 2);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(dV + head + (size_t)kwu * HD, nkb);
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(dK + head + (size_t)kwu * HD, nkb);
+        const int vo = (4 * g * HD + l32) * 2;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                asm volatile("s_nop 15\n\ts_nop 7" : "+a"(dv[kb][db]), "+a"(dk[kb][db]));
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int so = (32 * kb + 8 * (r >> 2)) * HD * 2;
+                    const int io = ((r & 3) * HD + db * 32) * 2;
+                    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(short, (__bf16)dv[kb][db][r]), rv,
+                                                          vo + io, so, 0);
+                    __builtin_amdgcn_raw_buffer_store_b16(
+                        __builtin_bit_cast(short, (__bf16)(dk[kb][db][r] * scale)), rk, vo + io, so, 0);
+                }
+            }
+    }
 }
 
 // ----------------------------------------------------------------------------
