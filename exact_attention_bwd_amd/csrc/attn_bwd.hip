@@ -989,15 +989,23 @@ void bwd_dq_kernel(const __bf16* __restrict__ Kimg, const __bf16* __restrict__ d
     }
     vm_wait<0>(kb[0]);                           // no copy into LDS outlives the workgroup
 
-    // ---- dQ = scale * acc, bf16 (RNE); rows past the end are not stored
-    __bf16* dQh = dQ + (size_t)bh * N * HD;
+    // ---- dQ = scale * acc, bf16 (RNE), through a buffer resource over the
+    //      pair's rows (rows past the end fall outside it and are dropped):
+    //      element r of block t is row 32 (qb0 + t) + 8 (r / 4) + 4 g + r % 4
+    //      of the pair, column 32 db + l32
     const int l32 = lane & 31;
+    const int q0u = __builtin_amdgcn_readfirstlane(q0);
+    const __amdgpu_buffer_rsrc_t rq =
+        make_rsrc(dQ + (size_t)bh * N * HD + (size_t)q0u * HD,
+                  __builtin_amdgcn_readfirstlane(max(0, min(2 * BR, N - q0u)) * HD * 2));
+    const int vo = (4 * g * HD + db * 32 + l32) * 2;
 #pragma unroll
     for (int t = 0; t < TQ; ++t) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int row = q0 + (qb0 + t) * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-            if (row < N) dQh[(size_t)row * HD + db * 32 + l32] = (__bf16)(acc[t][r] * scale);
+            const int so = ((qb0 + t) * 32 + 8 * (r >> 2)) * HD * 2;
+            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(short, (__bf16)(acc[t][r] * scale)), rq,
+                                                  vo + (r & 3) * HD * 2, so, 0);
         }
     }
 }
