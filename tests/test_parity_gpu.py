@@ -169,6 +169,21 @@ def test_outputs_are_deterministic(lib, name):
         assert torch.equal(a[n], b[n]), n
 
 
+def test_caller_stream_is_used(lib):
+    """Every launch goes on the stream the caller passes (here a second,
+    default-priority torch stream made current): the results equal those of a
+    run on the default stream bit for bit."""
+    import torch
+    cfg = next(c for c in RAGGED if c.name == "ragged_c128")
+    inp = make_dense_inputs(cfg)
+    a = _gpu_path(lib, inp, cfg)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        b = _gpu_path(lib, inp, cfg)
+    for n in ("o", "lse", "D", "dq", "dk", "dv"):
+        assert torch.equal(a[n], b[n]), n
+
+
 FULL = ["headline", "long8k", "long16k"]
 
 
