@@ -46,17 +46,18 @@ __all__ = [
     "causal_allowed", "scores", "row_logsumexp", "softmax_rows",
     "attention_forward", "bwd_preprocess", "softmax_backward",
     "attention_backward", "topk_allowed", "sparse_forward", "sparse_backward",
-    "gqa_forward", "gqa_backward",
+    "gqa_forward", "gqa_backward", "attention_backward_sampled",
 ]
 
 
 # ----------------------------------------------------------------------------
 # Masks
 # ----------------------------------------------------------------------------
-def causal_allowed(n_q: int, n_k: int) -> np.ndarray:
+def causal_allowed(n_q: int, n_k: int, row0: int = 0) -> np.ndarray:
     """Boolean [n_q, n_k]: True where key j may be seen by query i (j <= i,
-    top-left aligned; the pages only use n_q == n_k)."""
-    i = np.arange(n_q)[:, None]
+    top-left aligned; the pages only use n_q == n_k).  Rows are the queries
+    row0 .. row0 + n_q - 1 (a block of a taller mask)."""
+    i = np.arange(row0, row0 + n_q)[:, None]
     j = np.arange(n_k)[None, :]
     return j <= i
 
@@ -168,6 +169,58 @@ def attention_backward(q, k, v, do, scale: float, causal: bool = False, allowed=
     dq = scale * (ds @ k)
     dk = scale * (np.swapaxes(ds, -1, -2) @ q)
     return {"dq": dq, "dk": dk, "dv": dv, "D": D, "o": o, "lse": lse}
+
+
+def attention_backward_sampled(q, k, v, do, scale: float, causal: bool, rows, keys,
+                               chunk: int = 1024):
+    """The definitions of ``attention_backward`` for one (batch, head), kept to
+    selected outputs: O, L, D and dQ of the query rows ``rows``, dK and dV of
+    the keys ``keys``.  q, k, v, do: [N, d].  S and P are formed in blocks of
+    ``chunk`` query rows (each row's softmax is complete inside its block), so
+    no N x N matrix is held; the arithmetic per element is the same as in
+    ``attention_backward``: P by plain softmax of S, D from the exact O,
+    dS = P o (dP - D), dQ = scale * dS K, dK = scale * dS^T Q, dV = P^T dO.
+    Returns a dict of float64 arrays: o, lse, D, dq [len(rows), ...] and
+    dk, dv [len(keys), d]."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    n = q.shape[0]
+    rows = np.asarray(rows, dtype=np.int64)
+    keys = np.asarray(keys, dtype=np.int64)
+    D = np.empty(n)
+    o_rows = np.zeros((rows.size, v.shape[1]))
+    lse_rows = np.empty(rows.size)
+    dq_rows = np.zeros((rows.size, k.shape[1]))
+    dk = np.zeros((keys.size, q.shape[1]))
+    dv = np.zeros((keys.size, do.shape[1]))
+
+    def block(r0, r1):
+        allowed = causal_allowed(r1 - r0, n, row0=r0) if causal else None
+        s = scores(q[r0:r1], k, scale, allowed)
+        return s, softmax_rows(s)
+
+    # every row's O (for D); the selected rows' O and L
+    for r0 in range(0, n, chunk):
+        r1 = min(n, r0 + chunk)
+        s, p = block(r0, r1)
+        o = p @ v
+        D[r0:r1] = bwd_preprocess(o, do[r0:r1])
+        sel = np.nonzero((rows >= r0) & (rows < r1))[0]
+        o_rows[sel] = o[rows[sel] - r0]
+        lse_rows[sel] = row_logsumexp(s[rows[sel] - r0])
+    # dS block by block: the selected keys' dK, dV and the selected rows' dQ
+    for r0 in range(0, n, chunk):
+        r1 = min(n, r0 + chunk)
+        _, p = block(r0, r1)
+        dp = do[r0:r1] @ v.T
+        ds = softmax_backward(p, dp, D[r0:r1])
+        dv += p[:, keys].T @ do[r0:r1]
+        dk += scale * (ds[:, keys].T @ q[r0:r1])
+        sel = np.nonzero((rows >= r0) & (rows < r1))[0]
+        dq_rows[sel] = scale * (ds[rows[sel] - r0] @ k)
+    return {"o": o_rows, "lse": lse_rows, "D": D[rows], "dq": dq_rows, "dk": dk, "dv": dv}
 
 
 # ----------------------------------------------------------------------------

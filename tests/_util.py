@@ -96,3 +96,85 @@ def assert_lse(gpu, ref):
     err = float(np.max(np.abs(gpu - ref))) if ref.size else 0.0
     say(f"  lse: max_abs={err:.3e}")
     assert err <= LSE_ABS, err
+
+
+class Accum:
+    """The parity metrics of one output tensor accumulated piece by piece
+    (e.g. head by head), so that a full-size tensor is never held twice."""
+
+    def __init__(self, name):
+        self.name = name
+        self.err_sum = 0.0
+        self.ref_sum = 0.0
+        self.err_max = 0.0
+        self.ref_max = 0.0
+        self.n = 0
+
+    def add(self, gpu, ref):
+        assert gpu.shape == ref.shape, (self.name, gpu.shape, ref.shape)
+        assert np.all(np.isfinite(gpu)), f"{self.name}: non-finite values"
+        err = np.abs(gpu - ref)
+        self.err_sum += float(np.sum(err))
+        self.ref_sum += float(np.sum(np.abs(ref)))
+        if err.size:
+            self.err_max = max(self.err_max, float(np.max(err)))
+            self.ref_max = max(self.ref_max, float(np.max(np.abs(ref))))
+        self.n += gpu.size
+
+    def check(self):
+        if self.ref_max == 0.0:
+            say(f"  {self.name}: reference is exactly 0, max|gpu|={self.err_max:.3e}")
+            assert self.err_max <= ZERO_ABS, (self.name, self.err_max)
+            return
+        max_rel = self.err_max / self.ref_max
+        mean_rel = self.err_sum / max(self.ref_sum, 1e-300)
+        say(f"  {self.name}: {self.n} elements, max_rel={max_rel:.3e} (<= {MAX_REL:.0e}) "
+            f"mean_rel={mean_rel:.3e} (<= {MEAN_REL:.0e})")
+        assert max_rel <= MAX_REL, (self.name, max_rel)
+        assert mean_rel <= MEAN_REL, (self.name, mean_rel)
+
+
+class LseAccum:
+    def __init__(self):
+        self.err = 0.0
+
+    def add(self, gpu, ref):
+        assert np.all(np.isfinite(gpu))
+        if ref.size:
+            self.err = max(self.err, float(np.max(np.abs(gpu - ref))))
+
+    def check(self):
+        say(f"  lse: max_abs={self.err:.3e}")
+        assert self.err <= LSE_ABS, self.err
+
+
+# Exact identities of the backward (the attention-backward page, Appendix B,
+# "Softmax Backward Derivation": rows of dS sum to zero, and D = rowsum(P o dP)
+# = rowsum(dO o O)), over one head:
+#   sum_j dK_j = 0,  sum_j dV_j = sum_i dO_i,  sum Q o dQ = sum K o dK,
+#   sum V o dV = sum_i D_i.
+# Each residual is divided by the random-walk size of its summands,
+# sqrt(sum of their squares): per-element errors of relative size rho with
+# no common sign move a sum by about rho times that, so the residuals of
+# results within the parity bar (rho = 5e-3) stay below 5 rho = 2.5e-2 (the
+# column identities are averaged over the head-dim columns, as an RMS).  A
+# missing or zero tile of dQ, dK or dV, or a wrong mask, gives 0.1 to 1; a
+# 2 % scale error in dQ or dK about 2e-2.
+INV_BARS = {"sum_dk": 2.5e-2, "sum_dv": 2.5e-2, "qdq_kdk": 2.5e-2, "vdv_D": 2.5e-2}
+
+
+def head_invariants(q, k, v, do, dq, dk, dv, D):
+    """Residuals of the four identities for one head (float64 [N, d] arrays, D [N])."""
+    def cols(s, ss):                            # RMS over columns of |sum| / sqrt(sum of squares)
+        return float(np.sqrt(np.mean(s * s / np.maximum(ss, 1e-300))))
+
+    def scalar(a, b):                           # sum a = sum b
+        return abs(float(np.sum(a)) - float(np.sum(b))) / max(
+            float(np.sqrt(np.sum(a * a) + np.sum(b * b))), 1e-300)
+
+    return {
+        "sum_dk": cols(dk.sum(0), (dk * dk).sum(0)),
+        "sum_dv": cols(dv.sum(0) - do.sum(0), (dv * dv).sum(0) + (do * do).sum(0)),
+        "qdq_kdk": scalar(q * dq, k * dk),
+        "vdv_D": scalar(v * dv, D),
+    }

@@ -114,6 +114,31 @@ def test_sparse_backward_matches_finite_differences():
         assert _rel(g[name], _fd_grad(loss, x)) < 1e-7, name
 
 
+def test_sparse_unsorted_repeated_lists():
+    """Index lists in any order and with a repeated key: the backward still
+    matches finite differences of the forward, and the forward weighs a key
+    named twice by two (a gather over slots), as the closed form says."""
+    rng = np.random.default_rng(17)
+    hq, nq, nkv, dqk, dv = 2, 4, 5, 4, 3
+    q, k, v, do = _rand(rng, hq, nq, dqk), _rand(rng, nkv, dqk), _rand(rng, nkv, dv), _rand(rng, hq, nq, dv)
+    idx = np.array([[3, 0, 3, -1], [4, 1, 2, 1], [2, 2, 2, 0], [0, 4, 1, 3]], dtype=np.int32)
+    cnt = np.array([3, 4, 4, 2], dtype=np.int32)
+    scale = 0.7
+    g = oracle.sparse_backward(q, k, v, do, idx, cnt, scale)
+
+    def loss():
+        o, _ = oracle.sparse_forward(q, k, v, idx, cnt, scale)
+        return float(np.sum(do * o))
+
+    for name, x in (("dq", q), ("dk", k), ("dv", v)):
+        assert _rel(g[name], _fd_grad(loss, x)) < 1e-7, name
+    o, lse = oracle.sparse_forward(q, k, v, idx, cnt, scale)
+    for h in range(hq):                          # row 0 names key 3 twice and key 0 once
+        e3, e0 = np.exp(scale * q[h, 0] @ k[3]), np.exp(scale * q[h, 0] @ k[0])
+        assert _rel(o[h, 0], (2 * e3 * v[3] + e0 * v[0]) / (2 * e3 + e0)) < 1e-13
+        assert abs(lse[h, 0] - np.log(2 * e3 + e0)) < 1e-13
+
+
 # ----------------------------------------------------------------------------
 # library routine: PyTorch CPU float64 attention + autograd
 # ----------------------------------------------------------------------------
@@ -145,6 +170,29 @@ def test_against_torch_cpu_fp64(causal, n, d):
         *(torch.tensor(x) for x in (q, k, v)), 0.0, causal, scale=scale)[:2]
     assert np.max(np.abs(lse - lse_t.numpy())) < 1e-10
     assert np.max(np.abs(g["lse"] - lse_t.numpy())) < 1e-10
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_sampled_outputs_against_torch_cpu_fp64(causal):
+    """The blockwise, selected-output form of the backward (used where a full
+    N x N oracle is too large) against PyTorch's fp64 attention with autograd,
+    with blocks smaller than N and selected rows and keys on block edges."""
+    rng = np.random.default_rng(4242 + causal)
+    n, d, chunk = 150, 32, 64
+    q, k, v, do = (_rand(rng, n, d) for _ in range(4))
+    scale = 1.0 / math.sqrt(d)
+    rows = np.array([0, 1, 63, 64, 65, 127, 128, 149])
+    keys = np.array([0, 5, 63, 64, 100, 148, 149])
+    g = oracle.attention_backward_sampled(q, k, v, do, scale, causal, rows, keys, chunk=chunk)
+    o_t, dq_t, dk_t, dv_t = _torch_ref(q[None], k[None], v[None], do[None], scale, causal)
+    o_t, dq_t, dk_t, dv_t = o_t[0], dq_t[0], dk_t[0], dv_t[0]
+    assert _rel(g["o"], o_t[rows]) < 1e-12
+    assert _rel(g["dq"], dq_t[rows]) < 1e-10
+    assert _rel(g["dk"], dk_t[keys]) < 1e-10
+    assert _rel(g["dv"], dv_t[keys]) < 1e-10
+    assert _rel(g["D"], np.sum(do * o_t, -1)[rows]) < 1e-12
+    full = oracle.attention_backward(q, k, v, do, scale, causal=causal)
+    assert np.max(np.abs(g["lse"] - full["lse"][rows])) < 1e-12
 
 
 def test_sparse_against_torch_masked():

@@ -8,8 +8,10 @@ same seeded bf16 inputs, element by element.
   backward error is not masked by the forward;
 * full-size workloads (the headline causal B8 H16 N4096 d128 case and the long
   non-causal N=8192/16384 cases): the whole GPU path is run at full size in
-  the same launch configuration the benchmark times, and sampled heads are
-  compared element by element with the oracle.
+  the same launch configuration the benchmark times; every head of the
+  N <= 8192 cases is compared element by element with the oracle, the
+  N = 16384 case on sampled rows and keys of every head (and one whole head),
+  and the exact identities of the backward are checked on every head.
 """
 import math
 
@@ -18,7 +20,8 @@ import pytest
 
 import oracle
 from attn_inputs import DENSE_CONFIGS, DenseConfig, bf16_bits_to_f64, f32_to_bf16_bits, make_dense_inputs
-from _util import assert_close, assert_lse, f64_to_dev_bf16, from_dev, say, to_dev, torch_bf16_floor
+from _util import (INV_BARS, Accum, LseAccum, assert_close, assert_lse, f64_to_dev_bf16, from_dev,
+                   head_invariants, say, to_dev, torch_bf16_floor)
 
 pytestmark = pytest.mark.gpu
 
@@ -170,33 +173,124 @@ def test_outputs_are_deterministic(lib, name):
 
 
 def test_caller_stream_is_used(lib):
-    """Every launch goes on the stream the caller passes (here a second,
-    default-priority torch stream made current): the results equal those of a
-    run on the default stream bit for bit."""
+    """Every launch goes on the stream the caller passes.  A second,
+    default-priority stream is kept busy by a bounded spin kernel queued
+    ahead of the calls: right after them that stream still has work queued
+    while the default stream has none (work on the default stream would wait
+    for the spin and leave it busy too); after synchronising, the results
+    equal those of a run on the default stream bit for bit."""
     import torch
     cfg = next(c for c in RAGGED if c.name == "ragged_c128")
     inp = make_dense_inputs(cfg)
     a = _gpu_path(lib, inp, cfg)
+    q, k, v, do = (to_dev(inp[n]) for n in ("q", "k", "v", "do"))
+    torch.cuda.synchronize()
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
-        b = _gpu_path(lib, inp, cfg)
+        torch.cuda._sleep(100_000_000)           # bounded spin, tens of ms
+        o, lse = lib.attn_fwd(q, k, v, cfg.causal, cfg.scale)
+        D = lib.attn_bwd_preprocess(o, do)
+        dq, dk, dv = lib.attn_bwd(q, k, v, do, lse, D, cfg.causal, cfg.scale)
+        stream_busy = not s.query()
+        default_idle = torch.cuda.default_stream().query()
+    torch.cuda.synchronize()
+    assert stream_busy, "the caller's stream finished before its spin kernel could have"
+    assert default_idle, "work was queued on the default stream"
+    b = {"o": o, "lse": lse, "D": D, "dq": dq, "dk": dk, "dv": dv}
     for n in ("o", "lse", "D", "dq", "dk", "dv"):
         assert torch.equal(a[n], b[n]), n
 
 
-FULL = ["headline", "long8k", "long16k"]
+# ----------------------------------------------------------------------------
+# Full-size workloads, in the launch configuration the benchmark times.  The
+# GPU path runs once per workload (cached); the tests below then compare its
+# outputs with the oracle head by head, or on sampled rows and keys where a
+# whole head is too large for the oracle, and check the exact identities of
+# the backward on every head.
+# ----------------------------------------------------------------------------
+_FULL = {}
 
 
-@pytest.mark.parametrize("name", FULL)
-def test_full_size_sampled_heads(lib, name):
-    cfg = DENSE_CONFIGS[name]
+def _full_run(lib, name):
+    import torch
+    if name not in _FULL:
+        _FULL.clear()
+        cfg = DENSE_CONFIGS[name]
+        say(f"[parity-full] {name} B{cfg.B} H{cfg.H} N{cfg.N} d{cfg.d} causal={cfg.causal}: gpu")
+        inp = make_dense_inputs(cfg)
+        out = _gpu_path(lib, inp, cfg)
+        for n in ("o", "lse", "D", "dq", "dk", "dv"):
+            assert not torch.isnan(out[n]).any().item(), f"{n} has NaN (unwritten sentinel)"
+        BH = cfg.B * cfg.H
+        host = {n: t.cpu().reshape((BH,) + tuple(t.shape[2:])) for n, t in out.items()}
+        del out
+        torch.cuda.empty_cache()
+        _FULL[name] = (cfg, inp, host)
+    return _FULL[name]
+
+
+def _head(inp, cfg, n, h):
     BH = cfg.B * cfg.H
-    heads = sorted({0, BH // 2 + 1, BH - 1})
-    say(f"[parity-full] {name} B{cfg.B} H{cfg.H} N{cfg.N} d{cfg.d} causal={cfg.causal} heads={heads}")
-    inp = make_dense_inputs(cfg)
-    out = _gpu_path(lib, inp, cfg)
-    for n in ("o", "lse", "D", "dq", "dk", "dv"):
-        import torch
-        assert not torch.isnan(out[n]).any().item(), f"{n} has NaN (unwritten sentinel)"
-    say("  gpu done; oracle on sampled heads")
-    _compare(out, _oracle_heads(inp, cfg, heads), cfg, heads)
+    return bf16_bits_to_f64(inp[n].reshape(BH, cfg.N, cfg.d)[h])
+
+
+def _dev_head(host, n, h):
+    return from_dev(host[n][h])
+
+
+def _chunks(n_heads, parts):
+    return [list(range(n_heads * p // parts, n_heads * (p + 1) // parts)) for p in range(parts)]
+
+
+FULL_CASES = ([("headline", "heads", p, 4) for p in range(4)] + [("headline", "identities", 0, 1)]
+              + [("long8k", "heads", p, 2) for p in range(2)] + [("long8k", "identities", 0, 1)]
+              + [("long16k", "sampled", p, 2) for p in range(2)] + [("long16k", "identities", 0, 1)])
+
+
+@pytest.mark.parametrize("name,kind,part,parts", FULL_CASES, ids=lambda x: str(x))
+def test_full_size(lib, name, kind, part, parts):
+    """kind "heads": every element of O, L, D, dQ, dK, dV of every head (in
+    `parts` groups of heads, one test each).  kind "sampled" (N = 16384, where
+    a whole head is large for the oracle): for every head, 48 query rows (O,
+    L, D, dQ) and 48 keys (dK, dV) spread over the sequence, each from the
+    whole row or column of S (blockwise), and one whole head element by
+    element.  kind "identities": the exact identities of the backward on
+    every head (see head_invariants)."""
+    cfg, inp, host = _full_run(lib, name)
+    BH = cfg.B * cfg.H
+    if kind == "identities":
+        worst = {n: 0.0 for n in INV_BARS}
+        for h in range(BH):
+            q, k, v, do = (_head(inp, cfg, n, h) for n in ("q", "k", "v", "do"))
+            r = head_invariants(q, k, v, do, *(_dev_head(host, n, h) for n in ("dq", "dk", "dv", "D")))
+            for n, x in r.items():
+                worst[n] = max(worst[n], x)
+        say(f"  worst residuals over {BH} heads: " + ", ".join(f"{n} {x:.2e}" for n, x in worst.items()))
+        for n, x in worst.items():
+            assert x <= INV_BARS[n], (n, x)
+        return
+    heads = _chunks(BH, parts)[part]
+    rng = np.random.default_rng(cfg.N + part)
+    acc = {n: Accum(n) for n in ("o", "D", "dq", "dk", "dv")}
+    lse = LseAccum()
+    say(f"[parity-full] {name} heads {heads[0]}..{heads[-1]}: oracle ({kind})")
+    for h in heads:
+        q, k, v, do = (_head(inp, cfg, n, h) for n in ("q", "k", "v", "do"))
+        if kind == "heads" or h == heads[0] + 3:
+            ref = oracle.attention_backward(q, k, v, do, cfg.scale, causal=cfg.causal)
+            for n in acc:
+                acc[n].add(_dev_head(host, n, h), ref[n])
+            lse.add(_dev_head(host, "lse", h), ref["lse"])
+            continue
+        edges = np.array([0, 1, 63, 64, 127, 128, 255, 256, cfg.N - 65, cfg.N - 64, cfg.N - 2, cfg.N - 1])
+        rows = np.unique(np.concatenate([edges, rng.choice(cfg.N, 36, replace=False)]))
+        keys = np.unique(np.concatenate([edges, rng.choice(cfg.N, 36, replace=False)]))
+        ref = oracle.attention_backward_sampled(q, k, v, do, cfg.scale, cfg.causal, rows, keys, chunk=2048)
+        for n in ("o", "D", "dq"):
+            acc[n].add(_dev_head(host, n, h)[rows], ref[n])
+        for n in ("dk", "dv"):
+            acc[n].add(_dev_head(host, n, h)[keys], ref[n])
+        lse.add(_dev_head(host, "lse", h)[rows], ref["lse"])
+    for a in acc.values():
+        a.check()
+    lse.check()
