@@ -38,7 +38,7 @@ class AttnError(RuntimeError):
 def _load():
     if not os.path.exists(lib_path):
         raise ImportError(
-            f"{lib_path} is missing: build it first (python -m exact_attention_bwd_amd.build)")
+            f"{lib_path} is missing: build it first (python exact_attention_bwd_amd/build.py)")
     lib = ctypes.CDLL(lib_path, mode=ctypes.RTLD_GLOBAL)
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
@@ -53,6 +53,8 @@ def _load():
     lib.attn_bwd_timed.restype = i
     lib.attn_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
     lib.attn_fwd_gqa.restype = i
+    lib.attn_bwd_workspace_bytes_ex.argtypes = [i, i, i, i, i, i]
+    lib.attn_bwd_workspace_bytes_ex.restype = sz
     lib.attn_bwd_gqa_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.attn_bwd_gqa_workspace_bytes.restype = sz
     lib.attn_bwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, f, vp]
@@ -111,6 +113,16 @@ def _same(shape, x: torch.Tensor, name: str):
         raise ValueError(f"{name} has shape {tuple(x.shape)}, expected {shape}")
 
 
+def _workspace(workspace, need: int, like: torch.Tensor):
+    """The caller's workspace (any dtype) or a new one; it must be a contiguous
+    tensor on the same device as the inputs.  Returns (tensor, size in bytes)."""
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=like.device)
+    if not workspace.is_cuda or workspace.device != like.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
 def _stat(x: torch.Tensor, shape3, name: str):
     if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous() or tuple(x.shape) != shape3:
         raise ValueError(f"{name} must be a contiguous float32 device tensor of shape {shape3}")
@@ -147,8 +159,14 @@ def attn_bwd_preprocess(o, do, D=None, stream=None):
     return D
 
 
-def attn_bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
-    return int(_lib.attn_bwd_workspace_bytes(B, H, N, d))
+def attn_bwd_workspace_bytes(B: int, H: int, N: int, d: int, causal: bool | None = None,
+                             Hkv: int | None = None) -> int:
+    """Workspace bytes of attn_bwd (attn_bwd_gqa with Hkv): the exact size for
+    `causal`, or with causal=None a size that serves both."""
+    hkv = H if Hkv is None else Hkv
+    if causal is None:
+        return int(_lib.attn_bwd_gqa_workspace_bytes(B, H, hkv, N, d))
+    return int(_lib.attn_bwd_workspace_bytes_ex(B, H, hkv, N, d, int(bool(causal))))
 
 
 def attn_bwd(q, k, v, do, lse, D, causal: bool, scale: float | None = None,
@@ -170,10 +188,7 @@ def attn_bwd(q, k, v, do, lse, D, causal: bool, scale: float | None = None,
     dv = torch.empty_like(v) if dv is None else dv
     for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
         _same(shape, t, n)
-    need = attn_bwd_workspace_bytes(B, H, N, d)
-    if workspace is None:
-        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
-    ws_bytes = workspace.numel() * workspace.element_size()
+    workspace, ws_bytes = _workspace(workspace, attn_bwd_workspace_bytes(B, H, N, d, causal), q)
     if main_events is None:
         _check(_lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(D), _ptr(dq),
                              _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, B, H, N, d,
@@ -232,10 +247,7 @@ def attn_bwd_gqa(q, k, v, do, lse, D, causal: bool, scale: float | None = None,
     _same((B, H, N, d), dq, "dq")
     _same((B, Hkv, N, d), dk, "dk")
     _same((B, Hkv, N, d), dv, "dv")
-    need = attn_bwd_gqa_workspace_bytes(B, H, Hkv, N, d)
-    if workspace is None:
-        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
-    ws_bytes = workspace.numel() * workspace.element_size()
+    workspace, ws_bytes = _workspace(workspace, attn_bwd_workspace_bytes(B, H, N, d, causal, Hkv), q)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(D), _ptr(dq), _ptr(dk), _ptr(dv),
             _ptr(workspace), ws_bytes, B, H, Hkv, N, d, int(bool(causal)), float(scale), _stream(stream))
     if main_events is None:
@@ -313,10 +325,7 @@ def attn_sparse_bwd(q, k, v, do, lse, D, idx, topk_len=None, scale: float | None
     _dev(dq, torch.bfloat16, (Hq, Nq, dqk), "dq")
     _dev(dk, torch.bfloat16, (Nkv, dqk), "dk")
     _dev(dv, torch.bfloat16, (Nkv, dvd), "dv")
-    need = attn_sparse_bwd_workspace_bytes(Hq, Nq, Nkv, topk, dqk, dvd)
-    if workspace is None:
-        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
-    ws_bytes = workspace.numel() * workspace.element_size()
+    workspace, ws_bytes = _workspace(workspace, attn_sparse_bwd_workspace_bytes(Hq, Nq, Nkv, topk, dqk, dvd), q)
     args = [_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(D), _ptr(idx), _ptr(topk_len),
             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, Hq, Nq, Nkv, dqk, dvd, topk,
             float(scale), _stream(stream)]

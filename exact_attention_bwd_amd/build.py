@@ -1,6 +1,7 @@
 """Build the HIP library ``libattn_mi355x.so`` in-tree for gfx950.
 
-Usage: ``python -m exact_attention_bwd_amd.build`` (or ``build()`` from Python).
+Usage: ``python exact_attention_bwd_amd/build.py`` (or ``__graft_entry__.build()``);
+this file imports nothing from the package, so it runs before the library exists.
 Each ``csrc/*.hip`` file is compiled to an object with hipcc, in parallel, and
 the objects are linked into the shared library next to this file.
 """

@@ -177,6 +177,13 @@ __device__ __forceinline__ void gload16(bf16x8& d, const void* base, uint32_t vo
     asm volatile("global_load_dwordx4 %0, %1, %2 offset:%3" : "=&v"(d) : "v"(voff), "s"(base), "n"(OFF));
 }
 
+// gload16 that misses the CU's L1 (data other CUs wrote during the kernel)
+template <int OFF>
+__device__ __forceinline__ void gload16_l2(bf16x8& d, const void* base, uint32_t voff) {
+    static_assert(OFF >= 0 && OFF < 4096, "global offset field");
+    asm volatile("global_load_dwordx4 %0, %1, %2 offset:%3 sc0" : "=&v"(d) : "v"(voff), "s"(base), "n"(OFF));
+}
+
 // s_waitcnt vmcnt(N), tied to the eight registers whose loads it completes
 template <int N>
 __device__ __forceinline__ void vm_wait(bf16x8* r) {

@@ -103,11 +103,17 @@ attn_status attn_bwd_preprocess(const void* o, const void* dO, float* D, int B, 
                       "attn_bwd_preprocess launch");
 }
 
-size_t attn_bwd_gqa_workspace_bytes(int B, int H, int Hkv, int N, int d) {
+size_t attn_bwd_workspace_bytes_ex(int B, int H, int Hkv, int N, int d, int causal) {
     bool empty = false;
     if (check_shape(B, H, N, d, &empty) != ATTN_OK || empty) return 0;
     if (check_heads(H, Hkv) != ATTN_OK) return 0;
-    return attn::bwd_workspace_bytes(B * H, H / Hkv, N, d);
+    return attn::bwd_workspace_bytes(B * H, H / Hkv, N, d, causal != 0);
+}
+
+size_t attn_bwd_gqa_workspace_bytes(int B, int H, int Hkv, int N, int d) {
+    const size_t a = attn_bwd_workspace_bytes_ex(B, H, Hkv, N, d, 0);
+    const size_t b = attn_bwd_workspace_bytes_ex(B, H, Hkv, N, d, 1);
+    return a > b ? a : b;
 }
 
 size_t attn_bwd_workspace_bytes(int B, int H, int N, int d) {
@@ -134,7 +140,7 @@ attn_status attn_bwd_gqa_timed(const void* q, const void* k, const void* v, cons
     CHECK(check_ptr(dk, "dk", 16));
     CHECK(check_ptr(dv, "dv", 16));
     CHECK(check_ptr(workspace, "workspace", 16));
-    const size_t need = attn::bwd_workspace_bytes(B * H, H / Hkv, N, d);
+    const size_t need = attn::bwd_workspace_bytes(B * H, H / Hkv, N, d, causal != 0);
     if (workspace_bytes < need)
         return fail(ATTN_ERR_WORKSPACE, "workspace is %zu bytes, %zu needed", workspace_bytes, need);
     return hip_status(attn::launch_bwd(q, k, v, dO, lse, D, dq, dk, dv, workspace, B * H, H, H / Hkv,

@@ -84,7 +84,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(float* __restrict__ Lb,
                                                        float* __restrict__ Dp,
                                                        const float* __restrict__ lse,
                                                        const float* __restrict__ D, int BH, int N,
-                                                       int n_pad) {
+                                                       int n_pad, int* __restrict__ ctrl, int n_ctrl,
+                                                       int n_zero) {
     const long long rows = (long long)BH * n_pad;
     for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < rows;
          i += (long long)gridDim.x * 256) {
@@ -94,6 +95,9 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(float* __restrict__ Lb,
         Lb[i] = in ? lse[bh * N + n] * kLog2e : __builtin_inff();
         Dp[i] = in ? -D[bh * N + n] : 0.f;       // -D: added to dP in the kernels
     }
+    // the fused kernel's control block: n_zero zeros, then "no tile yet"
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < n_ctrl; i += gridDim.x * 256)
+        ctrl[i] = i < n_zero ? 0 : 0x7fffffff;
 }
 
 // Grouped-query attention with the query heads of a group split over NS
@@ -163,8 +167,22 @@ __device__ __forceinline__ int dst_lds_chunk(int c) {
     return c ^ ((((c >> 6) & 1) << 3) | (((c >> 5) & 1) << 2));
 }
 
-__device__ __forceinline__ size_t dst_tile(int bh, int i, int j, int tr, int tc) {
-    return ((size_t)((size_t)bh * tr + i) * tc + j) * DST_EL;
+// dS tiles of a (batch*head) are stored row after row of query tiles i; when
+// causal only the tiles with j <= i / 2 (the lower triangle: every 128-key
+// tile that reaches a row of the 64-row tile i) have a slot, i / 2 + 1 per
+// row, so row i starts at sum_{i' < i} (i' / 2 + 1) = (a + 1)(a + b) for
+// i = 2 a + b.
+__host__ __device__ __forceinline__ long long dst_row0(int i, bool causal, int tc) {
+    const long long a = i >> 1, b = i & 1;
+    return causal ? (a + 1) * (a + b) : (long long)i * tc;
+}
+
+__host__ __device__ __forceinline__ long long dst_tiles_per_head(int tr, int tc, bool causal) {
+    return dst_row0(tr, causal, tc);
+}
+
+__device__ __forceinline__ size_t dst_tile(int bh, int i, int j, int tr, int tc, bool causal) {
+    return ((size_t)bh * dst_tiles_per_head(tr, tc, causal) + dst_row0(i, causal, tc) + j) * DST_EL;
 }
 
 // Workspace image of K_j as ready-made B operands of dQ = dS K: for each
@@ -379,7 +397,7 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         // not also wait for them
         __syncthreads();
         const __amdgpu_buffer_rsrc_t dsr =
-            make_rsrc(dSw + dst_tile(hq0 + gq, it, j, tr_count, tc), DST_EL * 2);
+            make_rsrc(dSw + dst_tile(hq0 + gq, it, j, tr_count, tc, CAUSAL), DST_EL * 2);
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ds0), dsr,
                                                dst_run(qh, kw >> 1, kw & 1, 0) + lane * 16, 0, 0);
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ds1), dsr,
@@ -448,21 +466,51 @@ struct Smem2 {
     static_assert(BC2 * HD * 2 <= off_v, "K staging must fit below V");
 };
 
+// Causal 256-key tiles have (N - 256 j) / 64 query tiles.  Workgroups are
+// dealt round-robin over the 8 XCDs (hardware index b runs on XCD b % 8);
+// each XCD takes every eighth head and works through them two at a time,
+// longest tiles first within each pair.  That balances the work like a
+// global longest-first order while only about four heads' Q / dO are in use
+// on an XCD at once (its L2 holds them).  Other head counts: all heads' tile 0
+// first, then tile 1, ...  Non-causal tiles are equal; consecutive tiles of a
+// head go to the same XCD.
 template <bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(NW2 * 64, NW2 * 64), amdgpu_waves_per_eu(1, 1)))
-void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
-                         const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
-                         const float* __restrict__ Lb, const float* __restrict__ Dp,
-                         __bf16* __restrict__ dSw, __bf16* __restrict__ Kimg,
-                         __bf16* __restrict__ dK, __bf16* __restrict__ dV, int BH, int H, int G, int NS,
-                         float* __restrict__ part, int N,
-                         int n_pad, float scale) {
+__device__ __forceinline__ void w64_grid_item(int b, int BH, int tc2, int& bh, int& j) {
+    if (CAUSAL && BH % 16 == 0) {
+        const int x = b % 8, t = b / 8;
+        const int grp = t / (2 * tc2), r = t % (2 * tc2);
+        j = r / 2;
+        bh = (2 * grp + (r & 1)) * 8 + x;
+    } else if (CAUSAL) {
+        bh = b % BH;
+        j = b / BH;
+    } else {
+        const int logical = xcd_remap(b, BH * tc2);
+        bh = logical / tc2;
+        j = logical % tc2;
+    }
+}
+
+// One work item of the d = 128 dK/dV kernel: key tile j (256 keys) of the
+// grid row `bh` (a K / V head, times NS parts of its query heads).  FUSED:
+// the item is part of the persistent causal kernel below; its dS stores stay
+// cacheable (the same XCD reads them back within a few tiles) and, after
+// every fourth query tile, it publishes in prog[bh * tc2 + j] the lowest
+// query tile whose dS tiles are all stored.
+template <bool CAUSAL, bool FUSED>
+__device__ __forceinline__ void dkdv_w64_item(char* smem, const __bf16* __restrict__ Q,
+                                              const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+                                              const __bf16* __restrict__ dO, const float* __restrict__ Lb,
+                                              const float* __restrict__ Dp, __bf16* __restrict__ dSw,
+                                              __bf16* __restrict__ Kimg, __bf16* __restrict__ dK,
+                                              __bf16* __restrict__ dV, int BH, int H, int G, int NS,
+                                              float* __restrict__ part, int N, int n_pad, float scale,
+                                              int bh, int j, int* __restrict__ prog) {
     constexpr int HD = 128;
     using S = Smem2;
     constexpr int KSD = HD / 16;                 // 8 k steps over the head dim
     constexpr int DB = HD / 32;                  // 4 column blocks
     constexpr int TILE_EL = BR * HD;
-    extern __shared__ __attribute__((aligned(16))) char smem[];
 
     const int lane = threadIdx.x & 63;
     const int w = wave_id();
@@ -475,28 +523,6 @@ void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict_
     const int tc2 = (N + BC2 - 1) / BC2;
     const int tc = (N + BC - 1) / BC;            // 128-key tiles (dS and K image format)
     const int tr_count = (N + BR - 1) / BR;
-    // causal: key tile j has (N - 256 j) / 64 query tiles.  Workgroups are
-    // dealt round-robin over the 8 XCDs (hardware index b runs on XCD b % 8);
-    // each XCD takes every eighth head and works through them two at a time,
-    // longest tiles first within each pair.  That balances the work like a
-    // global longest-first order while only about four heads' Q / dO are in
-    // use on an XCD at once (its L2 holds them).  Other head counts: all
-    // heads' tile 0 first, then tile 1, ...  Non-causal tiles are equal;
-    // consecutive tiles of a head go to the same XCD.
-    int bh, j;
-    if (CAUSAL && BH % 16 == 0) {
-        const int x = blockIdx.x % 8, t = blockIdx.x / 8;
-        const int grp = t / (2 * tc2), r = t % (2 * tc2);
-        j = r / 2;
-        bh = (2 * grp + (r & 1)) * 8 + x;
-    } else if (CAUSAL) {
-        bh = blockIdx.x % BH;
-        j = blockIdx.x / BH;
-    } else {
-        const int logical = xcd_remap(blockIdx.x, BH * tc2);
-        bh = logical / tc2;
-        j = logical % tc2;
-    }
     const int k0 = j * BC2;
     const int kw0 = k0 + 64 * w;                 // this wave's first key
 
@@ -606,9 +632,11 @@ void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict_
             stage_tile((step + 1) / nt, tr_count - 1 - (step + 1) % nt, buf ^ 1);
         const __bf16* Qs = reinterpret_cast<const __bf16*>(smem + S::off_q) + buf * TILE_EL;
         const float* Ls = reinterpret_cast<const float*>(smem + S::off_l) + buf * BR;
-        // dS stores go nowhere (buffer records 0) for a 128-key half past N
+        // dS stores go nowhere (buffer records 0) for a 128-key half past N,
+        // or above the diagonal when causal (no slot: every entry is masked)
+        const bool st_ok = jst < tc && (!CAUSAL || jst <= it / 2);
         const __amdgpu_buffer_rsrc_t dsr =
-            make_rsrc(dSw + dst_tile(hq0 + gq, it, min(jst, tc - 1), tr_count, tc), jst < tc ? DST_EL * 2 : 0);
+            make_rsrc(dSw + dst_tile(hq0 + gq, it, st_ok ? jst : 0, tr_count, tc, CAUSAL), st_ok ? DST_EL * 2 : 0);
         // transposing-read bases of this tile: Q buffer + lane offset for the
         // 4 column blocks x 2 row halves; dO, the row half qb and k4 are
         // immediate offsets
@@ -782,10 +810,12 @@ void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict_
                 if constexpr (m >= 2 && m < 6) {
                     // run (sk, k4) = (0, 0) (1, 0) (0, 1) (1, 1) of this wave's block
                     constexpr int sk = m & 1, k4 = (m - 2) >> 1;
-                    // non-temporal: this kernel never reads dS back, and
-                    // the tiles should not push the shared Q / dO out of L2
+                    // non-temporal when a second kernel reads dS much
+                    // later: the tiles should not push the shared Q / dO
+                    // out of L2.  FUSED reads them back within a few tiles.
                     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, da[sk][k4]), dsr,
-                                                           dst_run(qb, w & 1, sk, k4) + lane * 16, 0, 2);
+                                                           dst_run(qb, w & 1, sk, k4) + lane * 16, 0,
+                                                           FUSED ? 0 : 2);
                 }
                 mfma_a(dk[kb][t & 3], da[kb][t >> 2], cat_u(tb[t][0], tb[t][1]));
                 // the next half's L and Q operands, after the last wait
@@ -793,7 +823,16 @@ void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict_
                 __builtin_amdgcn_sched_barrier(0);
             });
         });
+        if constexpr (FUSED) {
+            // every wave's dS stores of this tile have completed (in the
+            // L2 this XCD shares) before the barrier
+            if (it % 4 == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
         __syncthreads();                         // next tile landed; this one free
+        if constexpr (FUSED) {
+            if (it % 4 == 0 && threadIdx.x == 0)
+                __hip_atomic_store(prog + (size_t)bh * tc2 + j, it, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
 
     // ---- epilogue: dV, dK (scaled) of this wave's 64 keys, each pair of
@@ -849,6 +888,21 @@ void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict_
                 }
             }
     }
+}
+
+template <bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW2 * 64, NW2 * 64), amdgpu_waves_per_eu(1, 1)))
+void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+                         const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
+                         const float* __restrict__ Lb, const float* __restrict__ Dp,
+                         __bf16* __restrict__ dSw, __bf16* __restrict__ Kimg,
+                         __bf16* __restrict__ dK, __bf16* __restrict__ dV, int BH, int H, int G, int NS,
+                         float* __restrict__ part, int N, int n_pad, float scale) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    int bh, j;
+    w64_grid_item<CAUSAL>(blockIdx.x, BH, (N + BC2 - 1) / BC2, bh, j);
+    dkdv_w64_item<CAUSAL, false>(smem, Q, K, V, dO, Lb, Dp, dSw, Kimg, dK, dV, BH, H, G, NS, part, N,
+                                 n_pad, scale, bh, j, nullptr);
 }
 
 // ----------------------------------------------------------------------------
@@ -924,7 +978,7 @@ void bwd_dq_kernel(const __bf16* __restrict__ Kimg, const __bf16* __restrict__ d
             const int Ib = I % (DS_B / 1024);
             const bool ok = t2 == 0 || has_i1;
             const __amdgpu_buffer_rsrc_t r =
-                make_rsrc(dSw + dst_tile(bh, ok ? i0 + t2 : i0, jj, tr_count, tc), ok ? DS_B : 0);
+                make_rsrc(dSw + dst_tile(bh, ok ? i0 + t2 : i0, jj, tr_count, tc, CAUSAL), ok ? DS_B : 0);
             bdma16(r, dst_lds_chunk(Ib * 64 + lane) * 16, smem + st * STB + I * 1024);
         }
     };
@@ -1010,6 +1064,238 @@ void bwd_dq_kernel(const __bf16* __restrict__ Kimg, const __bf16* __restrict__ d
     }
 }
 
+// ----------------------------------------------------------------------------
+// Fused causal backward for d = 128 with one query head per K / V head: one
+// persistent kernel in which each work item is a 256-key tile j of a head.
+// The item runs the dK/dV loop above (which stores every dS tile of its keys),
+// then forms dQ for the four 64-row query tiles 4 j .. 4 j + 3 of the same
+// head: dQ_i = scale * sum over 128-key tiles jt <= i / 2 of dS_{i,jt} K_jt.
+// Those dS tiles come from the items j' <= j of the head, which walk the
+// query tiles from the last one down and so pass tiles 4 j .. 4 j + 3 one
+// step before item j finishes its own loop: the tiles are read back from the
+// cache while it still holds them, instead of by a second kernel after the
+// whole 2 GB at the headline shape has gone to memory and back.
+//
+// Work queues: head bh belongs to queue bh % 8, and a workgroup takes items
+// only from the queue of the XCD it runs on (hardware register XCC_ID), so
+// every item of a head, and every read of what its items wrote, stays within
+// one XCD and its L2.  Items are claimed with an atomic ticket in a fixed
+// order: heads two at a time, key tiles heaviest (j = 0) first, the two heads'
+// tiles alternating.  Item j waits only for items j' < j of its head, which
+// come earlier in the same queue and were therefore claimed by workgroups
+// that are running or done: no item waits for one that has not started.
+// The wait is bounded; on the bound it sets a flag in the control block and
+// goes on.  A queue whose XCD ran none of the workgroups is swept, in queue
+// order, by the last workgroup to finish (it then computes those heads on
+// its own, so they too see only their own writes).
+//
+// Control block (ints at the start of the workspace, cleared by the prep
+// kernel): [0, 8) the queue tickets, [8] workgroups finished, [9] nonzero if
+// a wait reached its bound, [10] items taken by the final sweep; then
+// prog[bh * tc2 + j], the lowest query tile whose dS item j has stored (a
+// multiple of 4; INT_MAX before its first).
+// ----------------------------------------------------------------------------
+constexpr int FQ = 4;                            // query tiles whose dQ an item forms
+constexpr int F_DS_B = DST_EL * 2;               // one dS tile (bytes)
+constexpr int F_STB = FQ * F_DS_B;               // one dQ stage: FQ tiles of one 128-key tile
+constexpr int F_CTRL = 64;                       // ints of the control block before prog
+constexpr int F_WAIT_LIMIT = 1 << 22;            // polls (about 0.1 us each) before giving up
+
+struct FusedSmem {
+    static constexpr int body = Smem2::bytes > 2 * F_STB ? Smem2::bytes : 2 * F_STB;
+    static constexpr int ticket = body;          // the claimed ticket, broadcast to the waves
+    static constexpr int bytes = body + 16;
+};
+
+__device__ __forceinline__ int xcc_id() {
+    unsigned x;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
+    return (int)(x & 7);
+}
+
+// Buffer -> LDS copy that misses the CU's L1 (the data was written by other
+// CUs of this XCD during this kernel).
+__device__ __forceinline__ void bdma16_l2(__amdgpu_buffer_rsrc_t r, int voff, void* lds_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16,
+                                             voff, 0, 0, 1);
+}
+
+// dQ of the query tiles i0 .. i0 + FQ - 1 (rows past N dropped) of head bh,
+// from its dS tiles and K image.  Wave w owns head-dim columns 32 w .. + 31
+// and all 8 blocks of 32 rows; per 128-key tile the FQ dS tiles are copied
+// into one of two LDS stages (the next tile's copy runs during this one's
+// products) and read transposed (A operands); the wave's K image slice comes
+// into registers, also one tile ahead.
+__device__ __forceinline__ void fused_dq_phase(char* smem, const __bf16* __restrict__ Kimg,
+                                               const __bf16* __restrict__ dSw, __bf16* __restrict__ dQ,
+                                               int bh, int i0, int N, float scale) {
+    constexpr int HD = 128;
+    constexpr int TQ = 2 * FQ;                   // 32-row blocks
+    constexpr int KS = BC / 16;                  // k steps per 128-key tile
+    const int lane = threadIdx.x & 63;
+    const int w = wave_id();
+    const int db = w;
+    const int g = lane >> 5;
+    const int t16 = lane & 15;
+    const int hh = (lane >> 4) & 1;
+    const int s4 = t16 >> 2;
+    const int tc = (N + BC - 1) / BC;
+    const int tr_count = (N + BR - 1) / BR;
+    const int q_end = min(N, (i0 + FQ) * BR);    // one past the last row
+    const int jt_end = min(tc, (q_end - 1) / BC + 1);
+
+    // transposing reads of the A operand (dS, query rows x keys), as in the
+    // dQ kernel: block qb = t is tile t / 2 of the stage, its 32-row half t % 2
+    uint32_t tra[TQ][2];
+#pragma unroll
+    for (int t = 0; t < TQ; ++t)
+#pragma unroll
+        for (int h4 = 0; h4 < 2; ++h4) {
+            const int c = (t & 1) * 512 + hh * 64 + 32 * (t16 & 1) + g * 8 + h4 * 4 + s4;
+            tra[t][h4] = lds_addr(smem) + (uint32_t)((t >> 1) * F_DS_B + dst_lds_chunk(c) * 16 + ((t16 >> 1) & 1) * 8);
+        }
+    // wave w copies tile i0 + w of the FQ (zeros when it has no slot: past
+    // the last row tile, or above the diagonal)
+    const int iw = i0 + w;
+    auto stage = [&](int jt, int st) {
+        const bool ok = iw < tr_count && jt <= iw / 2;
+        const __amdgpu_buffer_rsrc_t r =
+            make_rsrc(dSw + dst_tile(bh, ok ? iw : 0, ok ? jt : 0, tr_count, tc, true), ok ? F_DS_B : 0);
+#pragma unroll
+        for (int k = 0; k < F_DS_B / 1024; ++k)
+            bdma16_l2(r, dst_lds_chunk(k * 64 + lane) * 16, smem + st * F_STB + w * F_DS_B + k * 1024);
+    };
+    const uint32_t kvo = (uint32_t)((db * KS * 64 + lane) * 16);
+    auto load_k = [&](int jt, bf16x8* kb) {
+        const __bf16* kt = Kimg + kimg_tile(bh, jt, tc, HD);
+        static_for<0, KS>([&](auto ksI) {
+            constexpr int ks = decltype(ksI)::value;
+            gload16_l2<(ks & 3) * 1024>(kb[ks], kt, kvo + (ks >> 2) * 4096);
+        });
+    };
+
+    bf16x8 kb[2][KS];
+    f32x16 acc[TQ];
+#pragma unroll
+    for (int t = 0; t < TQ; ++t) acc[t] = zero16();
+    stage(0, 0);
+    load_k(0, kb[0]);
+    auto step = [&](int jj, auto stI) {
+        constexpr int st = decltype(stI)::value;
+        vm_wait<0>(kb[st]);
+        __builtin_amdgcn_s_barrier();           // tile jj landed for every wave; the other stage is free
+        stage(min(jj + 1, jt_end - 1), st ^ 1);
+        load_k(min(jj + 1, jt_end - 1), kb[st ^ 1]);
+        if (jj >= jt_end) return;
+        u32x2 ta[KS][TQ][2];
+        auto issue = [&](auto ksI) {
+            constexpr int ks = decltype(ksI)::value;
+            constexpr int off = 256 * (ks & 1) + 2048 * ((ks >> 1) & 1) + 4096 * (ks >> 2);
+#pragma unroll
+            for (int t = 0; t < TQ; ++t)
+                tr_read2o<off>(ta[ks][t][0], ta[ks][t][1], tra[t][0] + st * F_STB, tra[t][1] + st * F_STB);
+        };
+        issue(std::integral_constant<int, 0>{});
+        static_for<0, KS>([&](auto ksI) {
+            constexpr int ks = decltype(ksI)::value;
+            if constexpr (ks + 1 < KS) issue(std::integral_constant<int, ks + 1>{});
+            constexpr int later = (ks + 1 < KS ? 1 : 0) * 2 * TQ;
+            static_for<0, TQ>([&](auto tI) {
+                constexpr int t = decltype(tI)::value;
+                lgkm_wait<later + 2 * (TQ - 1 - t)>(ta[ks][t][0], ta[ks][t][1]);
+                acc[t] = mfma32(cat_u(ta[ks][t][0], ta[ks][t][1]), kb[st][ks], acc[t]);
+            });
+        });
+    };
+    for (int jj = 0; jj < jt_end; jj += 2) {
+        step(jj, std::integral_constant<int, 0>{});
+        step(jj + 1, std::integral_constant<int, 1>{});
+    }
+    vm_wait<0>(kb[0]);                           // no copy into LDS outlives the phase
+
+    // ---- dQ = scale * acc, bf16, through a buffer resource over the rows
+    //      [i0 * 64, q_end): element r of block t is row 32 t + 8 (r / 4) +
+    //      4 g + r % 4 of the item's rows, column 32 db + lane % 32
+    const int l32 = lane & 31;
+    const int q0u = __builtin_amdgcn_readfirstlane(i0 * BR);
+    const __amdgpu_buffer_rsrc_t rq =
+        make_rsrc(dQ + (size_t)bh * N * HD + (size_t)q0u * HD,
+                  __builtin_amdgcn_readfirstlane(max(0, q_end - q0u) * HD * 2));
+    const int vo = (4 * g * HD + db * 32 + l32) * 2;
+#pragma unroll
+    for (int t = 0; t < TQ; ++t) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int so = (t * 32 + 8 * (r >> 2)) * HD * 2;
+            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(short, (__bf16)(acc[t][r] * scale)), rq,
+                                                  vo + (r & 3) * HD * 2, so, 0);
+        }
+    }
+    __syncthreads();                             // every wave is done with the stages
+}
+
+__global__ __attribute__((amdgpu_flat_work_group_size(NW2 * 64, NW2 * 64), amdgpu_waves_per_eu(1, 1)))
+void bwd_fused_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+                      const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
+                      const float* __restrict__ Lb, const float* __restrict__ Dp,
+                      __bf16* __restrict__ dSw, __bf16* __restrict__ Kimg, __bf16* __restrict__ dQ,
+                      __bf16* __restrict__ dK, __bf16* __restrict__ dV, int BH, int H, int N, int n_pad,
+                      float scale, int* __restrict__ ctrl) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    int* const prog = ctrl + F_CTRL;
+    int* const ticket = reinterpret_cast<int*>(smem + FusedSmem::ticket);
+    const int tc2 = (N + BC2 - 1) / BC2;
+
+    auto run_queue = [&](int q, bool sweep) {
+        const int nq = q < BH ? (BH - q + 7) / 8 : 0;       // heads q, q + 8, ...
+        const int n_items = (nq + 1) / 2 * 2 * tc2;
+        for (;;) {
+            if (threadIdx.x == 0)
+                *ticket = __hip_atomic_fetch_add(ctrl + q, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+            const int t = *ticket;
+            __syncthreads();                     // read by every wave before the next claim
+            if (t >= n_items) break;
+            const int p = t / (2 * tc2), r = t % (2 * tc2);
+            const int lh = 2 * p + (r & 1);
+            if (lh >= nq) continue;              // the missing second head of an odd last pair
+            const int bh = q + 8 * lh, j = r / 2;
+            if (sweep && threadIdx.x == 0)
+                __hip_atomic_fetch_add(ctrl + 10, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            dkdv_w64_item<true, true>(smem, Q, K, V, dO, Lb, Dp, dSw, Kimg, dK, dV, BH, H, 1, 1, nullptr, N,
+                                      n_pad, scale, bh, j, prog);
+            // dQ of query tiles 4 j .. 4 j + 3 needs every item j' < j of
+            // this head past tile 4 j (its own stores are complete: the loop
+            // ended in a barrier after waiting for them)
+            if (threadIdx.x == 0) {
+                int spins = 0;
+                for (int jp = 0; jp < j; ++jp) {
+                    while (__hip_atomic_load(prog + (size_t)bh * tc2 + jp, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT) > 4 * j) {
+                        __builtin_amdgcn_s_sleep(2);
+                        if (++spins >= F_WAIT_LIMIT) {
+                            __hip_atomic_store(ctrl + 9, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            break;
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+            fused_dq_phase(smem, Kimg, dSw, dQ, bh, 4 * j, N, scale);
+        }
+    };
+    run_queue(xcc_id(), false);
+    // the last workgroup to finish sweeps every queue (all but one that no
+    // workgroup of its XCD ran on are empty by then)
+    if (threadIdx.x == 0)
+        *ticket = __hip_atomic_fetch_add(ctrl + 8, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const bool last = *ticket == (int)gridDim.x - 1;
+    __syncthreads();
+    if (last)
+        for (int q = 0; q < 8; ++q) run_queue(q, true);
+}
+
 }  // namespace bwd
 
 // ----------------------------------------------------------------------------
@@ -1039,19 +1325,18 @@ hipError_t launch_bwd_preprocess(const void* o, const void* dO, float* D, int BH
     return hipGetLastError();
 }
 
-// Workspace: [Lb BH x n_pad fp32][D BH x n_pad fp32][dS tiles BH x T_r x T_c
-// x (BC x BR) bf16][K image BH / G x T_c x (BC x d) bf16][grouped-query
-// partials: 2 x NS x BH / G x N x d fp32, only when NS > 1] for BH query heads
-// and BH / G key / value heads.  Every dS tile the dQ kernel reads is written
-// by the dK/dV kernel first (causal: exactly the tiles with j <= i / 2), and so
-// is every K image tile and every partial.
+// Workspace, in order (each part 256-byte aligned): Lb and Dp (BH x n_pad
+// fp32 each), the dS tiles (BH x dst_tiles_per_head x (BC x BR) bf16: the
+// lower triangle when causal), the K image (BH / G x T_c x (BC x d) bf16) and,
+// only when a group's query heads are split over NS > 1 workgroups, the
+// grouped-query partials (2 x NS x BH / G x N x d fp32).  Every byte that is
+// read is written earlier in the same call.
 static size_t n_pad_of(int N) { return (size_t)((N + bwd::BR - 1) / bwd::BR) * bwd::BR; }
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // key tiles per K / V head of the dK/dV grid
 static int dkdv_tiles(int N, int d) {
-#ifndef ATTN_DKDV_W32
     if (d == 128) return (N + bwd::BC2 - 1) / bwd::BC2;
-#endif
     return (N + bwd::BC - 1) / bwd::BC;
 }
 
@@ -1069,13 +1354,33 @@ static int gqa_parts(int BHkv, int N, int d, int G) {
     return ns;
 }
 
-size_t bwd_workspace_bytes(int BH, int G, int N, int d) {
+struct WsLayout {
+    size_t ctrl, lb, dp, ds, kimg, part, total;
+    int n_ctrl;                                  // ints of the fused kernel's control block (0: none)
+};
+
+// The fused causal kernel serves d = 128 with one query head per K / V head.
+static bool use_fused(int G, int d, bool causal) { return false && causal && d == 128 && G == 1; }
+
+static WsLayout ws_layout(int BH, int G, int N, int d, bool causal) {
+    WsLayout w{};
     const size_t rows = (size_t)BH * n_pad_of(N);
-    const size_t tr = (N + bwd::BR - 1) / bwd::BR, tc = (N + bwd::BC - 1) / bwd::BC;
+    const int tr = (N + bwd::BR - 1) / bwd::BR, tc = (N + bwd::BC - 1) / bwd::BC;
     const int ns = gqa_parts(BH / G, N, d, G);
-    const size_t parts = ns > 1 ? 2 * (size_t)ns * (BH / G) * N * d * sizeof(float) : 0;
-    return 2 * rows * sizeof(float) + (size_t)BH * tr * tc * bwd::DST_EL * 2 +
-           (size_t)(BH / G) * tc * bwd::BC * d * 2 + parts;
+    size_t o = 0;
+    w.n_ctrl = use_fused(G, d, causal) ? bwd::F_CTRL + BH * ((N + bwd::BC2 - 1) / bwd::BC2) : 0;
+    w.ctrl = o; o = align256(o + (size_t)w.n_ctrl * sizeof(int));
+    w.lb = o;   o = align256(o + rows * sizeof(float));
+    w.dp = o;   o = align256(o + rows * sizeof(float));
+    w.ds = o;   o = align256(o + (size_t)BH * bwd::dst_tiles_per_head(tr, tc, causal) * bwd::DST_EL * 2);
+    w.kimg = o; o = align256(o + (size_t)(BH / G) * tc * bwd::BC * d * 2);
+    w.part = o; o = align256(o + (ns > 1 ? 2 * (size_t)ns * (BH / G) * N * d * sizeof(float) : 0));
+    w.total = o;
+    return w;
+}
+
+size_t bwd_workspace_bytes(int BH, int G, int N, int d, bool causal) {
+    return ws_layout(BH, G, N, d, causal).total;
 }
 
 // BHkv = B * H / G key / value heads (the dK/dV grid has BHkv * ns rows)
@@ -1084,8 +1389,7 @@ static hipError_t launch_dkdv(const void* q, const void* k, const void* v, const
                               const float* Lb, const float* Dp, __bf16* dSw, __bf16* kimg, void* dk,
                               void* dv, int BHkv, int H, int G, int ns, float* part, int N, int n_pad,
                               float scale, hipStream_t stream) {
-#ifndef ATTN_DKDV_W32
-    if (HD == 128) {
+    if constexpr (HD == 128) {
         using S2 = bwd::Smem2;
         auto kern = bwd::bwd_dkdv_w64_kernel<CAUSAL>;
         hipError_t e = hipFuncSetAttribute((const void*)kern,
@@ -1097,18 +1401,18 @@ static hipError_t launch_dkdv(const void* q, const void* k, const void* v, const
                            Lb, Dp, dSw, kimg, (__bf16*)dk, (__bf16*)dv, BHkv * ns, H, G, ns, part, N,
                            n_pad, scale);
         return hipGetLastError();
+    } else {
+        using S = bwd::Smem<HD>;
+        auto kern = bwd::bwd_dkdv_kernel<HD, CAUSAL>;
+        hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, S::bytes);
+        if (e != hipSuccess) return e;
+        const int tc = (N + bwd::BC - 1) / bwd::BC;
+        hipLaunchKernelGGL(kern, dim3(BHkv * ns * tc), dim3(bwd::NT), S::bytes, stream, (const __bf16*)q,
+                           (const __bf16*)k, (const __bf16*)v, (const __bf16*)dO, Lb, Dp, dSw, kimg,
+                           (__bf16*)dk, (__bf16*)dv, BHkv * ns, H, G, ns, part, N, n_pad, scale);
+        return hipGetLastError();
     }
-#endif
-    using S = bwd::Smem<HD>;
-    auto kern = bwd::bwd_dkdv_kernel<HD, CAUSAL>;
-    hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, S::bytes);
-    if (e != hipSuccess) return e;
-    const int tc = (N + bwd::BC - 1) / bwd::BC;
-    hipLaunchKernelGGL(kern, dim3(BHkv * ns * tc), dim3(bwd::NT), S::bytes, stream, (const __bf16*)q,
-                       (const __bf16*)k, (const __bf16*)v, (const __bf16*)dO, Lb, Dp, dSw, kimg,
-                       (__bf16*)dk, (__bf16*)dv, BHkv * ns, H, G, ns, part, N, n_pad, scale);
-    return hipGetLastError();
 }
 
 template <int HD, bool CAUSAL>
@@ -1141,6 +1445,35 @@ static hipError_t launch_pair(const void* q, const void* k, const void* v, const
     return launch_dq<HD, CAUSAL>(kimg, dSw, dq, BH, H, G, N, scale, stream);
 }
 
+static int device_cus() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
+static hipError_t launch_fused(const void* q, const void* k, const void* v, const void* dO,
+                               const float* Lb, const float* Dp, __bf16* dSw, __bf16* kimg, int* ctrl,
+                               void* dq, void* dk, void* dv, int BH, int H, int N, int n_pad, float scale,
+                               hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+    auto kern = bwd::bwd_fused_kernel;
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       bwd::FusedSmem::bytes);
+    if (e != hipSuccess) return e;
+    if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(device_cus()), dim3(bwd::NW2 * 64), bwd::FusedSmem::bytes, stream,
+                       (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dO, Lb, Dp, dSw,
+                       kimg, (__bf16*)dq, (__bf16*)dk, (__bf16*)dv, BH, H, N, n_pad, scale, ctrl);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
+    return hipSuccess;
+}
+
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* dO, const float* lse,
                       const float* D, void* dq, void* dk, void* dv, void* workspace, int BH, int H,
                       int G, int N, int d, bool causal, float scale, hipStream_t stream,
@@ -1148,16 +1481,21 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* d
     if ((long long)BH * N == 0) return hipSuccess;
     const int n_pad = (int)n_pad_of(N);
     const size_t rows = (size_t)BH * n_pad;
-    float* Lb = (float*)workspace;
-    float* Dp = Lb + rows;
-    __bf16* dSw = (__bf16*)(Dp + rows);
-    const size_t tr = (N + bwd::BR - 1) / bwd::BR, tc = (N + bwd::BC - 1) / bwd::BC;
-    __bf16* kimg = dSw + (size_t)BH * tr * tc * bwd::DST_EL;
-    float* part = (float*)(kimg + (size_t)(BH / G) * tc * bwd::BC * d);
+    const WsLayout w = ws_layout(BH, G, N, d, causal);
+    char* ws = (char*)workspace;
+    int* ctrl = (int*)(ws + w.ctrl);
+    float* Lb = (float*)(ws + w.lb);
+    float* Dp = (float*)(ws + w.dp);
+    __bf16* dSw = (__bf16*)(ws + w.ds);
+    __bf16* kimg = (__bf16*)(ws + w.kimg);
+    float* part = (float*)(ws + w.part);
     hipLaunchKernelGGL(bwd_prep_kernel, dim3(grid_for((long long)rows, 256, 4096)), dim3(256), 0,
-                       stream, Lb, Dp, lse, D, BH, N, n_pad);
+                       stream, Lb, Dp, lse, D, BH, N, n_pad, ctrl, w.n_ctrl, bwd::F_CTRL);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (use_fused(G, d, causal))
+        return launch_fused(q, k, v, dO, Lb, Dp, dSw, kimg, ctrl, dq, dk, dv, BH, H, N, n_pad, scale, stream,
+                            main_start, main_stop);
     if (d == 128)
         return causal ? launch_pair<128, true>(q, k, v, dO, Lb, Dp, dSw, kimg, part, dq, dk, dv, BH, H, G, N, n_pad, scale, stream, main_start, main_stop)
                       : launch_pair<128, false>(q, k, v, dO, Lb, Dp, dSw, kimg, part, dq, dk, dv, BH, H, G, N, n_pad, scale, stream, main_start, main_stop);

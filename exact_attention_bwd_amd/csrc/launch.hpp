@@ -15,7 +15,7 @@ hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, floa
 hipError_t launch_bwd_preprocess(const void* o, const void* dO, float* D, int BH, int N, int d,
                                  hipStream_t stream);
 
-size_t bwd_workspace_bytes(int BH, int G, int N, int d);
+size_t bwd_workspace_bytes(int BH, int G, int N, int d, bool causal);
 
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* dO, const float* lse,
                       const float* D, void* dq, void* dk, void* dv, void* workspace, int BH, int H,

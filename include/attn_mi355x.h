@@ -73,13 +73,24 @@ attn_status attn_bwd_preprocess(const void* o, const void* dO, float* D, int B, 
                                 int d, void* stream);
 
 /*
- * Size in bytes of the workspace attn_bwd needs: the row statistics L*log2(e)
- * and D padded to the 64-row query tile (2 x B*H*ceil(N/64)*64 fp32), one
- * bf16 128 x 64 dS^T tile per (batch*head, 64-row query tile, 128-key tile)
- * (B*H*ceil(N/64)*ceil(N/128)*16 KiB), and a bf16 copy of K rearranged as
- * matrix-core operands (B*H*ceil(N/128)*128*d*2 bytes).  0 when B*H*N == 0.
+ * Size in bytes of a workspace that serves attn_bwd for both values of
+ * `causal` (the larger of the two attn_bwd_workspace_bytes_ex sizes).  0 when
+ * B*H*N == 0 or the shape is unsupported.
  */
 size_t attn_bwd_workspace_bytes(int B, int H, int N, int d);
+
+/*
+ * Exact workspace size of attn_bwd / attn_bwd_gqa for this shape and masking
+ * (Hkv = H for attn_bwd): the row statistics L*log2(e) and D padded to the
+ * 64-row query tile (2 x B*H*ceil(N/64)*64 fp32); one bf16 128 x 64 dS tile per
+ * (batch*head, 64-row query tile i, 128-key tile j) -- for causal only the
+ * tiles with j <= i/2, the lower triangle; a bf16 copy of K rearranged as
+ * matrix-core operands (B*Hkv*ceil(N/128)*128*d*2 bytes); and, for grouped-
+ * query shapes whose query heads are split over several workgroups, fp32
+ * partials of dK and dV.  Each part is rounded up to 256 bytes.  0 when
+ * B*H*N == 0 or the shape is unsupported.
+ */
+size_t attn_bwd_workspace_bytes_ex(int B, int H, int Hkv, int N, int d, int causal);
 
 /*
  * Fused backward (attention-backward page: the tiled backward pseudocode and
@@ -94,7 +105,8 @@ size_t attn_bwd_workspace_bytes(int B, int H, int N, int d);
  *   D           : fp32 [B, H, N]  from attn_bwd_preprocess, read only
  *   dq, dk, dv  : bf16 [B, H, N, d], written
  *   workspace   : device scratch of at least attn_bwd_workspace_bytes(B,H,N,d)
- *                 bytes (its content on entry is ignored and on exit unspecified)
+ *                 bytes, or of attn_bwd_workspace_bytes_ex(B,H,H,N,d,causal) (its
+ *                 content on entry is ignored and on exit unspecified)
  *   causal, scale : as for attn_fwd (must match the forward that produced lse)
  * dQ, dK and dV are deterministic (bitwise reproducible for the same inputs).
  */
@@ -135,8 +147,9 @@ attn_status attn_bwd_timed(const void* q, const void* k, const void* v, const vo
 attn_status attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                          int H, int Hkv, int N, int d, int causal, float scale, void* stream);
 
-/* Workspace of attn_bwd_gqa: as attn_bwd_workspace_bytes(B, H, N, d) but with
- * the K image sized for the Hkv key / value heads.  0 for invalid shapes. */
+/* Workspace of attn_bwd_gqa that serves both values of `causal`:
+ * max over causal of attn_bwd_workspace_bytes_ex(B, H, Hkv, N, d, causal).
+ * 0 for invalid shapes. */
 size_t attn_bwd_gqa_workspace_bytes(int B, int H, int Hkv, int N, int d);
 
 /* Grouped-query backward: lse, D and dO per query head, dk / dv per K / V head. */

@@ -45,16 +45,34 @@ def test_library_is_gfx950_code(ea):
     assert "gfx950" in out
 
 
+def _ws_expected(B, H, N, d, causal):
+    """Row statistics (two fp32 per row, rows rounded up to 64), one bf16
+    128 x 64 dS tile per (head, 64-row query tile i, 128-key tile j) -- when
+    causal only j <= i // 2, counted here tile by tile -- and a bf16 image of K
+    per 128-key tile; each part rounded up to 256 bytes."""
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    tr, tc = -(-N // 64), -(-N // 128)
+    tiles = sum(min(tc, i // 2 + 1) if causal else tc for i in range(tr))
+    rows = B * H * tr * 64
+    return 2 * up(rows * 4) + up(B * H * tiles * 128 * 64 * 2) + up(B * H * tc * 128 * d * 2)
+
+
 def test_workspace_size(ea):
-    # two fp32 row statistics (rows rounded up to 64) + one bf16 128x64 dS^T
-    # tile per (batch*head, 64-row query tile, 128-key tile) + a bf16 image of K
-    # per 128-key tile
-    tile = 128 * 64 * 2
-    assert ea.attn_bwd_workspace_bytes(8, 16, 4096, 128) == (
-        2 * 128 * 4096 * 4 + 128 * 64 * 32 * tile + 128 * 32 * 128 * 128 * 2)
-    assert ea.attn_bwd_workspace_bytes(1, 1, 100, 64) == 2 * 128 * 4 + 2 * 1 * tile + 128 * 64 * 2
+    for B, H, N, d in ((8, 16, 4096, 128), (1, 1, 100, 64), (2, 3, 333, 128), (1, 2, 1, 64)):
+        for causal in (False, True):
+            assert ea.attn_bwd_workspace_bytes(B, H, N, d, causal) == _ws_expected(B, H, N, d, causal)
+        assert ea.attn_bwd_workspace_bytes(B, H, N, d) == _ws_expected(B, H, N, d, False)
+    # the causal lower triangle is about half the tiles at the headline shape
+    full, tri = (ea.attn_bwd_workspace_bytes(8, 16, 4096, 128, c) for c in (False, True))
+    assert 0.5 < tri / full < 0.55
     assert ea.attn_bwd_workspace_bytes(0, 16, 4096, 128) == 0
     assert ea.attn_bwd_workspace_bytes(1, 1, 128, 96) == 0                  # unsupported d
+
+
+def test_binding_rejects_host_workspace(ea):
+    import torch
+    with pytest.raises(ValueError, match="workspace"):
+        ea._workspace(torch.empty(64, dtype=torch.uint8), 16, torch.empty(1))
 
 
 def _raw(ea):
