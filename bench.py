@@ -82,9 +82,14 @@ def dense_metric(cfg, hkv=None):
 
 
 # The kernel that dominates a dense step, and the share of the conventional
-# FLOP count it performs: the dK/dV kernel forms S, dP, dV and dK (4 of the 5
-# products); the dQ kernel forms the fifth.
+# FLOP count it performs.  Causal d = 128 with one query head per K/V head:
+# the fused kernel forms all five products (S, dP, dV, dK, dQ); its timing
+# events also cover the one-workgroup sweep launched after it.  Otherwise the
+# dK/dV kernel forms S, dP, dV and dK (4 of the 5) and the dQ kernel the
+# fifth.
 def dominant_kernel(d, causal, gqa):
+    if d == 128 and causal and not gqa:
+        return "bwd_fused_kernel", 1.0
     if d == 128:
         return "bwd_dkdv_w64_kernel", 0.8
     return "bwd_dkdv_kernel", 0.8
@@ -357,7 +362,7 @@ def run_profile(out_dir, config, extra):
     for name, limit, prof, args in passes:
         cmd = ["timeout", "-s", "KILL", str(limit), "rocprofv3", *prof, "--output-format", "csv",
                "-d", os.path.join(out_dir, name), "-o", name, "--", *me, *args]
-        shown = " ".join(cmd).replace(ROOT, "$REPO").replace(out_dir, "OUT").replace(sys.executable, "python3")
+        shown = " ".join(cmd).replace(out_dir, "OUT").replace(ROOT, "$REPO").replace(sys.executable, "python3")
         commands.append(shown)
         print(f"[profile] {name}: start", flush=True)
         with open(os.path.join(out_dir, f"{name}.log"), "w") as log:

@@ -6,6 +6,7 @@
 #include <stdio.h>
 
 #include "../../include/attn_mi355x.h"
+#include "api_error.hpp"
 #include "launch.hpp"
 
 namespace {
@@ -65,6 +66,14 @@ attn_status check_ptr(const void* p, const char* name, uintptr_t align) {
     } while (0)
 
 }  // namespace
+
+attn_status attn::report(attn_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
 
 extern "C" {
 

@@ -491,6 +491,38 @@ __device__ __forceinline__ void w64_grid_item(int b, int BH, int tc2, int& bh, i
     }
 }
 
+constexpr int FQ = 4;                            // query tiles whose dQ an item forms
+constexpr int F_DS_B = DST_EL * 2;               // one dS tile (bytes)
+constexpr int F_CTRL = 64;                       // ints of the control block before prog
+constexpr int F_WAIT_LIMIT = 1 << 22;            // polls (about 0.1 us each) before giving up
+
+struct FusedSmem {
+    static constexpr int body = Smem2::bytes;    // the dQ stages overlay the dK/dV layout
+    static constexpr int ticket = body;          // the claimed ticket, broadcast to the waves
+    static constexpr int state = body + 16;      // the work loop's state across an item (8 ints)
+    static constexpr int bytes = body + 48;
+};
+
+// A value recomputed where it stands (an empty asm the compiler must keep in
+// place): in the persistent kernel below, per-lane and per-shape constants
+// derived from these would otherwise be hoisted out of its work loop and kept
+// live across both phases of every item, which the register file cannot hold.
+__device__ __forceinline__ int here_v(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+// this lane's index in its wave, computed from nothing (threadIdx.x need not
+// stay live across a persistent loop)
+__device__ __forceinline__ int lane_here() {
+    int x;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(x));
+    return x;
+}
+__device__ __forceinline__ int here_s(int x) {
+    asm volatile("" : "+s"(x));
+    return x;
+}
+
 // One work item of the d = 128 dK/dV kernel: key tile j (256 keys) of the
 // grid row `bh` (a K / V head, times NS parts of its query heads).  FUSED:
 // the item is part of the persistent causal kernel below; its dS stores stay
@@ -505,7 +537,7 @@ __device__ __forceinline__ void dkdv_w64_item(char* smem, const __bf16* __restri
                                               __bf16* __restrict__ Kimg, __bf16* __restrict__ dK,
                                               __bf16* __restrict__ dV, int BH, int H, int G, int NS,
                                               float* __restrict__ part, int N, int n_pad, float scale,
-                                              int bh, int j, int* __restrict__ prog) {
+                                              int bh, int j, int* __restrict__ prog, int wave) {
     constexpr int HD = 128;
     using S = Smem2;
     constexpr int KSD = HD / 16;                 // 8 k steps over the head dim
@@ -520,7 +552,6 @@ __device__ __forceinline__ void dkdv_w64_item(char* smem, const __bf16* __restri
     const int hh = (lane >> 4) & 1;
     const int s4 = t16 >> 2;
 
-    const int tc2 = (N + BC2 - 1) / BC2;
     const int tc = (N + BC - 1) / BC;            // 128-key tiles (dS and K image format)
     const int tr_count = (N + BR - 1) / BR;
     const int k0 = j * BC2;
@@ -830,8 +861,13 @@ __device__ __forceinline__ void dkdv_w64_item(char* smem, const __bf16* __restri
         }
         __syncthreads();                         // next tile landed; this one free
         if constexpr (FUSED) {
-            if (it % 4 == 0 && threadIdx.x == 0)
-                __hip_atomic_store(prog + (size_t)bh * tc2 + j, it, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (it % 4 == 0 && w == 0 && lane == 0) {
+                // the progress slot's address waits in LDS (no register
+                // holds it across the loop)
+                const int* st = reinterpret_cast<const int*>(smem + FusedSmem::state);
+                int* slot = reinterpret_cast<int*>(((uint64_t)(uint32_t)st[5] << 32) | (uint32_t)st[4]);
+                __hip_atomic_store(slot, it, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
         }
     }
 
@@ -871,7 +907,9 @@ __device__ __forceinline__ void dkdv_w64_item(char* smem, const __bf16* __restri
         const int nkb = __builtin_amdgcn_readfirstlane(max(0, min(64, N - kwu)) * HD * 2);
         const __amdgpu_buffer_rsrc_t rv = make_rsrc(dV + head + (size_t)kwu * HD, nkb);
         const __amdgpu_buffer_rsrc_t rk = make_rsrc(dK + head + (size_t)kwu * HD, nkb);
-        const int vo = (4 * g * HD + l32) * 2;
+        // FUSED: the lane recomputed here rather than kept live over the loop
+        const int le = FUSED ? lane_here() : lane;
+        const int vo = (4 * (le >> 5) * HD + (le & 31)) * 2;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -902,7 +940,7 @@ void bwd_dkdv_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict_
     int bh, j;
     w64_grid_item<CAUSAL>(blockIdx.x, BH, (N + BC2 - 1) / BC2, bh, j);
     dkdv_w64_item<CAUSAL, false>(smem, Q, K, V, dO, Lb, Dp, dSw, Kimg, dK, dV, BH, H, G, NS, part, N,
-                                 n_pad, scale, bh, j, nullptr);
+                                 n_pad, scale, bh, j, nullptr, 0);
 }
 
 // ----------------------------------------------------------------------------
@@ -1085,28 +1123,15 @@ void bwd_dq_kernel(const __bf16* __restrict__ Kimg, const __bf16* __restrict__ d
 // come earlier in the same queue and were therefore claimed by workgroups
 // that are running or done: no item waits for one that has not started.
 // The wait is bounded; on the bound it sets a flag in the control block and
-// goes on.  A queue whose XCD ran none of the workgroups is swept, in queue
-// order, by the last workgroup to finish (it then computes those heads on
-// its own, so they too see only their own writes).
+// goes on.  Tickets that no workgroup of their XCD took are processed by a
+// one-workgroup sweep kernel launched right after.
 //
 // Control block (ints at the start of the workspace, cleared by the prep
 // kernel): [0, 8) the queue tickets, [8] workgroups finished, [9] nonzero if
-// a wait reached its bound, [10] items taken by the final sweep; then
+// a wait reached its bound, [10] items taken by the sweep kernel; then
 // prog[bh * tc2 + j], the lowest query tile whose dS item j has stored (a
 // multiple of 4; INT_MAX before its first).
 // ----------------------------------------------------------------------------
-constexpr int FQ = 4;                            // query tiles whose dQ an item forms
-constexpr int F_DS_B = DST_EL * 2;               // one dS tile (bytes)
-constexpr int F_STB = FQ * F_DS_B;               // one dQ stage: FQ tiles of one 128-key tile
-constexpr int F_CTRL = 64;                       // ints of the control block before prog
-constexpr int F_WAIT_LIMIT = 1 << 22;            // polls (about 0.1 us each) before giving up
-
-struct FusedSmem {
-    static constexpr int body = Smem2::bytes > 2 * F_STB ? Smem2::bytes : 2 * F_STB;
-    static constexpr int ticket = body;          // the claimed ticket, broadcast to the waves
-    static constexpr int bytes = body + 16;
-};
-
 __device__ __forceinline__ int xcc_id() {
     unsigned x;
     asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
@@ -1120,20 +1145,38 @@ __device__ __forceinline__ void bdma16_l2(__amdgpu_buffer_rsrc_t r, int voff, vo
                                              voff, 0, 0, 1);
 }
 
+// s_waitcnt vmcnt(N) tied to the four registers (one 64-key step of K image
+// operands) whose loads it completes
+template <int N>
+__device__ __forceinline__ void vm_wait4(bf16x8* r) {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    asm volatile("s_waitcnt vmcnt(%[n])" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]) : [n] "n"(N) : "memory");
+}
+
 // dQ of the query tiles i0 .. i0 + FQ - 1 (rows past N dropped) of head bh,
-// from its dS tiles and K image.  Wave w owns head-dim columns 32 w .. + 31
-// and all 8 blocks of 32 rows; per 128-key tile the FQ dS tiles are copied
-// into one of two LDS stages (the next tile's copy runs during this one's
-// products) and read transposed (A operands); the wave's K image slice comes
-// into registers, also one tile ahead.
+// from its dS tiles and K image, in steps of 64 keys (half a 128-key dS
+// tile).  Wave w owns head-dim columns 32 w .. + 31 and all 8 blocks of 32
+// rows.  Each step copies the 64-key halves of the FQ dS tiles into one of
+// F_NST LDS stages (wave w copies tile i0 + w) and loads the wave's K image
+// slice into registers; the copies run F_NST - 1 steps ahead, so three
+// steps of dS and K are in flight while one is multiplied.  The A operands
+// (dS, query rows x keys) come from transposing LDS reads.
+constexpr int F_HB = F_DS_B / 2;                 // one 64-key half of a dS tile (8 KiB)
+constexpr int F_NST = 4;                         // dQ stages
+constexpr int F_STH = FQ * F_HB;                 // one stage: the halves of the FQ tiles (32 KiB)
+constexpr int F_STEP_VM = F_HB / 1024 + 4;       // vector-memory loads one step issues per wave
+static_assert(F_NST * F_STH <= Smem2::bytes, "dQ stages overlay the dK/dV layout");
+
 __device__ __forceinline__ void fused_dq_phase(char* smem, const __bf16* __restrict__ Kimg,
                                                const __bf16* __restrict__ dSw, __bf16* __restrict__ dQ,
-                                               int bh, int i0, int N, float scale) {
+                                               int bh, int i0, int N, float scale, int wave) {
     constexpr int HD = 128;
     constexpr int TQ = 2 * FQ;                   // 32-row blocks
-    constexpr int KS = BC / 16;                  // k steps per 128-key tile
-    const int lane = threadIdx.x & 63;
-    const int w = wave_id();
+    constexpr int KH = BC / 32;                  // k steps per 64-key half
+    // lane and wave recomputed here: shared with the dK/dV phase, their
+    // derived offsets would stay live across it
+    const int lane = lane_here();
+    const int w = here_s(wave);
     const int db = w;
     const int g = lane >> 5;
     const int t16 = lane & 15;
@@ -1142,76 +1185,100 @@ __device__ __forceinline__ void fused_dq_phase(char* smem, const __bf16* __restr
     const int tc = (N + BC - 1) / BC;
     const int tr_count = (N + BR - 1) / BR;
     const int q_end = min(N, (i0 + FQ) * BR);    // one past the last row
-    const int jt_end = min(tc, (q_end - 1) / BC + 1);
+    const int nh = 2 * min(tc, (q_end - 1) / BC + 1);   // 64-key steps
 
-    // transposing reads of the A operand (dS, query rows x keys), as in the
-    // dQ kernel: block qb = t is tile t / 2 of the stage, its 32-row half t % 2
-    uint32_t tra[TQ][2];
+    // Layout of a stage: tile t of the FQ at t * F_HB; in it, the 4 KiB block
+    // of 32-row half qh at qh * 4 KiB, holding the stored block (qh, key half
+    // wh) of the dS tile with the 16-byte chunks of each 1 KiB run permuted
+    // by dst_lds_chunk (as in the dQ kernel).  Transposing-read addresses for
+    // block t (tile t / 2, half t % 2) in stage 0; k step ks of the half adds
+    // 256 (ks & 1) + 2048 (ks >> 1) bytes, stage st adds st * F_STH.
+    // (the read offset field holds 16 bits: stages 2 and 3 read through a
+    // second set of bases, 64 KiB up)
+    uint32_t tra[2][TQ][2];
 #pragma unroll
     for (int t = 0; t < TQ; ++t)
 #pragma unroll
         for (int h4 = 0; h4 < 2; ++h4) {
-            const int c = (t & 1) * 512 + hh * 64 + 32 * (t16 & 1) + g * 8 + h4 * 4 + s4;
-            tra[t][h4] = lds_addr(smem) + (uint32_t)((t >> 1) * F_DS_B + dst_lds_chunk(c) * 16 + ((t16 >> 1) & 1) * 8);
+            const int c = (t & 1) * 256 + hh * 64 + 32 * (t16 & 1) + g * 8 + h4 * 4 + s4;
+            tra[0][t][h4] = lds_addr(smem) + (uint32_t)((t >> 1) * F_HB + dst_lds_chunk(c) * 16 + ((t16 >> 1) & 1) * 8);
+            tra[1][t][h4] = tra[0][t][h4] + 2 * F_STH;
         }
-    // wave w copies tile i0 + w of the FQ (zeros when it has no slot: past
-    // the last row tile, or above the diagonal)
+    static_assert(2 * F_STH == 65536, "stage bases");
+    // wave w copies the 64-key half of tile i0 + w (zeros when the tile has
+    // no slot: past the last row tile, or above the diagonal)
     const int iw = i0 + w;
-    auto stage = [&](int jt, int st) {
+    auto stage = [&](int jh, int st) {
+        const int jt = jh >> 1, wh = jh & 1;
         const bool ok = iw < tr_count && jt <= iw / 2;
         const __amdgpu_buffer_rsrc_t r =
             make_rsrc(dSw + dst_tile(bh, ok ? iw : 0, ok ? jt : 0, tr_count, tc, true), ok ? F_DS_B : 0);
 #pragma unroll
-        for (int k = 0; k < F_DS_B / 1024; ++k)
-            bdma16_l2(r, dst_lds_chunk(k * 64 + lane) * 16, smem + st * F_STB + w * F_DS_B + k * 1024);
+        for (int k = 0; k < F_HB / 1024; ++k) {
+            const int qh = k >> 2, run = k & 3;
+            bdma16_l2(r, dst_lds_chunk((2 * qh + wh) * 256 + run * 64 + lane) * 16,
+                      smem + st * F_STH + w * F_HB + qh * 4096 + run * 1024);
+        }
     };
-    const uint32_t kvo = (uint32_t)((db * KS * 64 + lane) * 16);
-    auto load_k = [&](int jt, bf16x8* kb) {
-        const __bf16* kt = Kimg + kimg_tile(bh, jt, tc, HD);
-        static_for<0, KS>([&](auto ksI) {
+    // the wave's K image slice of key half jh: 16-key steps 4 (jh & 1) ..
+    const uint32_t kvo = (uint32_t)((db * (BC / 16) * 64 + lane) * 16);
+    auto load_k = [&](int jh, bf16x8* kb) {
+        const __bf16* kt = Kimg + kimg_tile(bh, jh >> 1, tc, HD);
+        static_for<0, KH>([&](auto ksI) {
             constexpr int ks = decltype(ksI)::value;
-            gload16_l2<(ks & 3) * 1024>(kb[ks], kt, kvo + (ks >> 2) * 4096);
+            gload16_l2<ks * 1024>(kb[ks], kt, kvo + (jh & 1) * 4096);
         });
     };
 
-    bf16x8 kb[2][KS];
+    bf16x8 kb[F_NST][KH];
     f32x16 acc[TQ];
 #pragma unroll
     for (int t = 0; t < TQ; ++t) acc[t] = zero16();
-    stage(0, 0);
-    load_k(0, kb[0]);
-    auto step = [&](int jj, auto stI) {
+    // steps 0 .. F_NST - 2 in flight before the first; a step past the end
+    // reloads the last one, so every step issues the same loads
+    static_for<0, F_NST - 1>([&](auto sI) {
+        constexpr int s0 = decltype(sI)::value;
+        stage(min(s0, nh - 1), s0);
+        load_k(min(s0, nh - 1), kb[s0]);
+    });
+    auto step = [&](int jh, auto stI) {
         constexpr int st = decltype(stI)::value;
-        vm_wait<0>(kb[st]);
-        __builtin_amdgcn_s_barrier();           // tile jj landed for every wave; the other stage is free
-        stage(min(jj + 1, jt_end - 1), st ^ 1);
-        load_k(min(jj + 1, jt_end - 1), kb[st ^ 1]);
-        if (jj >= jt_end) return;
-        u32x2 ta[KS][TQ][2];
-        auto issue = [&](auto ksI) {
-            constexpr int ks = decltype(ksI)::value;
-            constexpr int off = 256 * (ks & 1) + 2048 * ((ks >> 1) & 1) + 4096 * (ks >> 2);
-#pragma unroll
-            for (int t = 0; t < TQ; ++t)
-                tr_read2o<off>(ta[ks][t][0], ta[ks][t][1], tra[t][0] + st * F_STB, tra[t][1] + st * F_STB);
+        constexpr int nx = (st + F_NST - 1) % F_NST;     // the stage of step jh + F_NST - 1
+        // this step's loads have landed (the F_NST - 2 later steps' remain)
+        vm_wait4<(F_NST - 2) * F_STEP_VM>(kb[st]);
+        __builtin_amdgcn_s_barrier();           // landed for every wave; stage nx is free
+        stage(min(jh + F_NST - 1, nh - 1), nx);
+        load_k(min(jh + F_NST - 1, nh - 1), kb[nx]);
+        if (jh >= nh) return;
+        // A operands: the step's first k step is read up front; after each
+        // product (ks, t) the reads of (ks + 1, t) are issued, so that 14
+        // reads (7 products' worth) are in flight behind the one waited for
+        u32x2 ta[KH][TQ][2];
+        auto rd = [&](auto ksI, auto tI) {
+            constexpr int ks = decltype(ksI)::value, t = decltype(tI)::value;
+            constexpr int off = (st & 1) * F_STH + 256 * (ks & 1) + 2048 * (ks >> 1);
+            tr_read2o<off>(ta[ks][t][0], ta[ks][t][1], tra[st >> 1][t][0], tra[st >> 1][t][1]);
         };
-        issue(std::integral_constant<int, 0>{});
-        static_for<0, KS>([&](auto ksI) {
+        static_for<0, TQ>([&](auto tI) { rd(std::integral_constant<int, 0>{}, tI); });
+        static_for<0, KH>([&](auto ksI) {
             constexpr int ks = decltype(ksI)::value;
-            if constexpr (ks + 1 < KS) issue(std::integral_constant<int, ks + 1>{});
-            constexpr int later = (ks + 1 < KS ? 1 : 0) * 2 * TQ;
             static_for<0, TQ>([&](auto tI) {
                 constexpr int t = decltype(tI)::value;
-                lgkm_wait<later + 2 * (TQ - 1 - t)>(ta[ks][t][0], ta[ks][t][1]);
+                // issued after (ks, t): (ks, t + 1 ..) and, but for the last
+                // k step, (ks + 1, .. t - 1)
+                lgkm_wait<ks + 1 < KH ? 2 * (TQ - 1) : 2 * (TQ - 1 - t)>(ta[ks][t][0], ta[ks][t][1]);
                 acc[t] = mfma32(cat_u(ta[ks][t][0], ta[ks][t][1]), kb[st][ks], acc[t]);
+                if constexpr (ks + 1 < KH) rd(std::integral_constant<int, ks + 1>{}, tI);
             });
         });
     };
-    for (int jj = 0; jj < jt_end; jj += 2) {
-        step(jj, std::integral_constant<int, 0>{});
-        step(jj + 1, std::integral_constant<int, 1>{});
+    for (int jh = 0; jh < nh; jh += F_NST) {
+        step(jh, std::integral_constant<int, 0>{});
+        step(jh + 1, std::integral_constant<int, 1>{});
+        step(jh + 2, std::integral_constant<int, 2>{});
+        step(jh + 3, std::integral_constant<int, 3>{});
     }
-    vm_wait<0>(kb[0]);                           // no copy into LDS outlives the phase
+    vm_wait4<0>(kb[0]);                          // no copy into LDS outlives the phase
 
     // ---- dQ = scale * acc, bf16, through a buffer resource over the rows
     //      [i0 * 64, q_end): element r of block t is row 32 t + 8 (r / 4) +
@@ -1234,66 +1301,138 @@ __device__ __forceinline__ void fused_dq_phase(char* smem, const __bf16* __restr
     __syncthreads();                             // every wave is done with the stages
 }
 
-__global__ __attribute__((amdgpu_flat_work_group_size(NW2 * 64, NW2 * 64), amdgpu_waves_per_eu(1, 1)))
-void bwd_fused_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
-                      const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
-                      const float* __restrict__ Lb, const float* __restrict__ Dp,
-                      __bf16* __restrict__ dSw, __bf16* __restrict__ Kimg, __bf16* __restrict__ dQ,
-                      __bf16* __restrict__ dK, __bf16* __restrict__ dV, int BH, int H, int N, int n_pad,
-                      float scale, int* __restrict__ ctrl) {
-    extern __shared__ __attribute__((aligned(16))) char smem[];
-    int* const prog = ctrl + F_CTRL;
-    int* const ticket = reinterpret_cast<int*>(smem + FusedSmem::ticket);
-    const int tc2 = (N + BC2 - 1) / BC2;
+// wave-uniform copies of a call's arguments (a call passes them in vector
+// registers)
+template <typename T>
+__device__ __forceinline__ T* uni(T* p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ float uni(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+}
 
-    auto run_queue = [&](int q, bool sweep) {
-        const int nq = q < BH ? (BH - q + 7) / 8 : 0;       // heads q, q + 8, ...
-        const int n_items = (nq + 1) / 2 * 2 * tc2;
-        for (;;) {
-            if (threadIdx.x == 0)
-                *ticket = __hip_atomic_fetch_add(ctrl + q, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __syncthreads();
-            const int t = *ticket;
-            __syncthreads();                     // read by every wave before the next claim
-            if (t >= n_items) break;
-            const int p = t / (2 * tc2), r = t % (2 * tc2);
-            const int lh = 2 * p + (r & 1);
-            if (lh >= nq) continue;              // the missing second head of an odd last pair
-            const int bh = q + 8 * lh, j = r / 2;
-            if (sweep && threadIdx.x == 0)
-                __hip_atomic_fetch_add(ctrl + 10, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            dkdv_w64_item<true, true>(smem, Q, K, V, dO, Lb, Dp, dSw, Kimg, dK, dV, BH, H, 1, 1, nullptr, N,
-                                      n_pad, scale, bh, j, prog);
-            // dQ of query tiles 4 j .. 4 j + 3 needs every item j' < j of
-            // this head past tile 4 j (its own stores are complete: the loop
-            // ended in a barrier after waiting for them)
-            if (threadIdx.x == 0) {
-                int spins = 0;
-                for (int jp = 0; jp < j; ++jp) {
-                    while (__hip_atomic_load(prog + (size_t)bh * tc2 + jp, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT) > 4 * j) {
-                        __builtin_amdgcn_s_sleep(2);
-                        if (++spins >= F_WAIT_LIMIT) {
-                            __hip_atomic_store(ctrl + 9, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                            break;
-                        }
-                    }
+struct FusedArgs {
+    const __bf16* Q;
+    const __bf16* K;
+    const __bf16* V;
+    const __bf16* dO;
+    const float* Lb;
+    const float* Dp;
+    __bf16* dSw;
+    __bf16* Kimg;
+    __bf16* dQ;
+    __bf16* dK;
+    __bf16* dV;
+    int* ctrl;
+    int BH, H, N, n_pad;
+    float scale;
+};
+
+// Claim the next ticket of queue q (wave 0 lane 0; broadcast through LDS)
+// and decode it: returns false once the queue is exhausted; `valid` is false
+// for the missing second head of an odd last pair.
+__device__ __forceinline__ bool fused_claim(char* smem, const FusedArgs& a, int q, int wave, int& bh, int& j,
+                                            bool& valid) {
+    int* const ticket = reinterpret_cast<int*>(smem + FusedSmem::ticket);
+    const int tc2 = (a.N + BC2 - 1) / BC2;
+    const int nq = q < a.BH ? (a.BH - q + 7) / 8 : 0;       // heads q, q + 8, ...
+    const int n_items = (nq + 1) / 2 * 2 * tc2;
+    if (wave == 0 && lane_here() == 0)
+        *ticket = __hip_atomic_fetch_add(a.ctrl + q, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int t = __builtin_amdgcn_readfirstlane(*ticket);
+    __syncthreads();                             // read by every wave before the slot is reused
+    if (t >= n_items) return false;
+    const int p = t / (2 * tc2), r = t % (2 * tc2);
+    const int lh = 2 * p + (r & 1);
+    valid = lh < nq;
+    bh = q + 8 * lh;
+    j = r / 2;
+    return true;
+}
+
+// One item: the dK/dV loop of key tile j of head bh (publishing its
+// progress), then, once every item j' < j of the head has stored the dS
+// tiles of query tiles 4 j .. 4 j + 3, the dQ of those tiles.
+__device__ __forceinline__ void fused_item(char* smem, const FusedArgs& a, int bh, int j, int wave) {
+    const int tc2 = (a.N + BC2 - 1) / BC2;
+    int* const st = reinterpret_cast<int*>(smem + FusedSmem::state);
+    if (wave == 0 && lane_here() == 0) {
+        const uint64_t slot = reinterpret_cast<uint64_t>(a.ctrl + F_CTRL + (size_t)bh * tc2 + j);
+        st[4] = (int)(uint32_t)slot;
+        st[5] = (int)(uint32_t)(slot >> 32);
+    }
+    __syncthreads();
+    dkdv_w64_item<true, true>(smem, a.Q, a.K, a.V, a.dO, a.Lb, a.Dp, a.dSw, a.Kimg, a.dK, a.dV, a.BH, a.H, 1, 1,
+                              nullptr, a.N, a.n_pad, a.scale, bh, j, nullptr, wave);
+    // its own stores are complete: the loop ended in a barrier after
+    // waiting for them
+    if (wave == 0 && lane_here() == 0) {
+        const int* prog = a.ctrl + F_CTRL + (size_t)bh * tc2;
+        int spins = 0;
+        for (int jp = 0; jp < j; ++jp) {
+            while (__hip_atomic_load(prog + jp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) > 4 * j) {
+                __builtin_amdgcn_s_sleep(2);
+                if (++spins >= F_WAIT_LIMIT) {
+                    __hip_atomic_store(a.ctrl + 9, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    break;
                 }
             }
-            __syncthreads();
-            fused_dq_phase(smem, Kimg, dSw, dQ, bh, 4 * j, N, scale);
         }
-    };
-    run_queue(xcc_id(), false);
-    // the last workgroup to finish sweeps every queue (all but one that no
-    // workgroup of its XCD ran on are empty by then)
-    if (threadIdx.x == 0)
-        *ticket = __hip_atomic_fetch_add(ctrl + 8, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     __syncthreads();
-    const bool last = *ticket == (int)gridDim.x - 1;
-    __syncthreads();
-    if (last)
-        for (int q = 0; q < 8; ++q) run_queue(q, true);
+    fused_dq_phase(smem, a.Kimg, a.dSw, a.dQ, bh, 4 * j, a.N, a.scale, wave);
+}
+
+// One item per workgroup: the workgroup claims the next ticket of its XCD's
+// queue when it starts, so tickets are taken in dispatch order and every
+// item an item waits for belongs to a workgroup that started earlier (and
+// runs, or is done).  The grid has as many workgroups per XCD as the
+// largest queue has items; surplus workgroups find their queue empty and
+// exit.  The workgroups check in as they finish (ctrl[8]).
+__global__ __attribute__((amdgpu_flat_work_group_size(NW2 * 64, NW2 * 64), amdgpu_waves_per_eu(1, 1)))
+void bwd_fused_kernel(FusedArgs args) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int wave = wave_id();
+    int bh = 0, j = 0;
+    bool valid = false;
+    if (fused_claim(smem, args, xcc_id(), wave, bh, j, valid) && valid) fused_item(smem, args, bh, j, wave);
+    if (wave == 0 && lane_here() == 0)
+        __hip_atomic_fetch_add(args.ctrl + 8, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Runs after bwd_fused_kernel, as one workgroup: any ticket still unclaimed
+// (a queue whose XCD ran fewer workgroups than it has items) is taken here,
+// in queue order, so its items' reads of dS see either this workgroup's own
+// stores or those of the kernel before (complete at the kernel boundary).
+// Normally every queue is already exhausted and this returns at once.  The
+// item runs behind a call so that the loop does not hold its registers.
+__device__ __noinline__ void fused_item_call(char* smem, const FusedArgs* a, int bh, int j, int wave) {
+    FusedArgs u;
+    u.Q = uni(a->Q); u.K = uni(a->K); u.V = uni(a->V); u.dO = uni(a->dO); u.Lb = uni(a->Lb); u.Dp = uni(a->Dp);
+    u.dSw = uni(a->dSw); u.Kimg = uni(a->Kimg); u.dQ = uni(a->dQ); u.dK = uni(a->dK); u.dV = uni(a->dV);
+    u.ctrl = uni(a->ctrl); u.BH = uni(a->BH); u.H = uni(a->H); u.N = uni(a->N); u.n_pad = uni(a->n_pad);
+    u.scale = uni(a->scale);
+    fused_item(uni(smem), u, uni(bh), uni(j), uni(wave));
+}
+
+__global__ __attribute__((amdgpu_flat_work_group_size(NW2 * 64, NW2 * 64), amdgpu_waves_per_eu(1, 1)))
+void bwd_fused_sweep_kernel(FusedArgs args) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int wave = wave_id();
+    for (int q = 0; q < 8; ++q) {
+        int bh = 0, j = 0;
+        bool valid = false;
+        while (fused_claim(smem, args, q, wave, bh, j, valid)) {
+            if (!valid) continue;
+            if (wave == 0 && lane_here() == 0)
+                __hip_atomic_fetch_add(args.ctrl + 10, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            fused_item_call(smem, &args, bh, j, wave);
+        }
+    }
 }
 
 }  // namespace bwd
@@ -1360,7 +1499,7 @@ struct WsLayout {
 };
 
 // The fused causal kernel serves d = 128 with one query head per K / V head.
-static bool use_fused(int G, int d, bool causal) { return false && causal && d == 128 && G == 1; }
+static bool use_fused(int G, int d, bool causal) { return causal && d == 128 && G == 1; }
 
 static WsLayout ws_layout(int BH, int G, int N, int d, bool causal) {
     WsLayout w{};
@@ -1445,30 +1584,25 @@ static hipError_t launch_pair(const void* q, const void* k, const void* v, const
     return launch_dq<HD, CAUSAL>(kimg, dSw, dq, BH, H, G, N, scale, stream);
 }
 
-static int device_cus() {
-    static int cus[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cus[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cus[dev] = n;
-    }
-    return cus[dev];
-}
-
 static hipError_t launch_fused(const void* q, const void* k, const void* v, const void* dO,
                                const float* Lb, const float* Dp, __bf16* dSw, __bf16* kimg, int* ctrl,
                                void* dq, void* dk, void* dv, int BH, int H, int N, int n_pad, float scale,
                                hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
-    auto kern = bwd::bwd_fused_kernel;
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       bwd::FusedSmem::bytes);
-    if (e != hipSuccess) return e;
+    for (const void* kern : {(const void*)bwd::bwd_fused_kernel, (const void*)bwd::bwd_fused_sweep_kernel}) {
+        hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bwd::FusedSmem::bytes);
+        if (e != hipSuccess) return e;
+    }
+    bwd::FusedArgs a{(const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dO, Lb, Dp, dSw, kimg,
+                     (__bf16*)dq, (__bf16*)dk, (__bf16*)dv, ctrl, BH, H, N, n_pad, scale};
+    // queue 0 holds the most heads (ceil(BH / 8)), taken in pairs
+    const int tc2 = (N + bwd::BC2 - 1) / bwd::BC2;
+    const int nq0 = (BH + 7) / 8;
+    const int per_xcd = (nq0 + 1) / 2 * 2 * tc2;
+    hipError_t e;
     if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(device_cus()), dim3(bwd::NW2 * 64), bwd::FusedSmem::bytes, stream,
-                       (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dO, Lb, Dp, dSw,
-                       kimg, (__bf16*)dq, (__bf16*)dk, (__bf16*)dv, BH, H, N, n_pad, scale, ctrl);
+    hipLaunchKernelGGL(bwd::bwd_fused_kernel, dim3(8 * per_xcd), dim3(bwd::NW2 * 64), bwd::FusedSmem::bytes, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd::bwd_fused_sweep_kernel, dim3(1), dim3(bwd::NW2 * 64), bwd::FusedSmem::bytes, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
     return hipSuccess;

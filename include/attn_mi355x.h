@@ -96,17 +96,25 @@ size_t attn_bwd_workspace_bytes_ex(int B, int H, int Hkv, int N, int d, int caus
  * Fused backward (attention-backward page: the tiled backward pseudocode and
  * section "Main backward kernel"): recomputes P = exp(scale*S - L) tile by tile
  * and forms dV = P^T dO, dP = dO V^T, dS = P o (dP - D), dQ = scale*dS K and
- * dK = scale*dS^T Q.  A first kernel (one workgroup per 128-key tile) produces
- * dK and dV and stores each bf16 dS tile in `workspace`; a second kernel (one
- * workgroup per 64-row query tile) reduces dQ = scale * sum_j dS_ij K_j in
- * fp32 registers.  Both run on `stream`; no atomics are used.
+ * dK = scale*dS^T Q.  Work is split by 256-key (d = 128) or 128-key (d = 64)
+ * tiles: each workgroup keeps its keys' dK and dV in registers over the query
+ * tiles and stores every bf16 dS tile in `workspace`; dQ_i = scale *
+ * sum_j dS_ij K_j is then reduced in fp32 registers, without atomics:
+ *  - causal, d = 128, H = Hkv: in the same kernel, by the workgroup of the
+ *    key tile on the diagonal of query tiles i, once the workgroups of the
+ *    earlier key tiles of that head have stored their dS tiles of those rows
+ *    (their progress is published in the workspace);
+ *  - otherwise: by a second, query-parallel kernel.
+ * All launches are on `stream`.
  *   q, k, v, dO : bf16 [B, H, N, d], read only
  *   lse         : fp32 [B, H, N]  L from attn_fwd (natural log), read only
  *   D           : fp32 [B, H, N]  from attn_bwd_preprocess, read only
  *   dq, dk, dv  : bf16 [B, H, N, d], written
  *   workspace   : device scratch of at least attn_bwd_workspace_bytes(B,H,N,d)
  *                 bytes, or of attn_bwd_workspace_bytes_ex(B,H,H,N,d,causal) (its
- *                 content on entry is ignored and on exit unspecified)
+ *                 content on entry is ignored and on exit unspecified; for the
+ *                 causal d = 128 path its first 64 ints are the work queues'
+ *                 counters and status words)
  *   causal, scale : as for attn_fwd (must match the forward that produced lse)
  * dQ, dK and dV are deterministic (bitwise reproducible for the same inputs).
  */
@@ -118,8 +126,10 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* dO
 /*
  * Same as attn_bwd, for profiling: when main_start / main_stop (hipEvent_t
  * created by the caller) are non-NULL they are recorded on `stream`
- * immediately before and after the dK/dV kernel (the dominant one), so the
- * caller can time it alone (hipEventElapsedTime) without a profiler.
+ * immediately before and after the dominant kernel (the fused kernel, with
+ * the one-workgroup sweep launched right after it, on the causal d = 128
+ * path; the dK/dV kernel otherwise), so the caller can time it alone
+ * (hipEventElapsedTime) without a profiler.
  */
 attn_status attn_bwd_timed(const void* q, const void* k, const void* v, const void* dO,
                            const float* lse, const float* D, void* dq, void* dk, void* dv,

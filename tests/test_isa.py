@@ -18,6 +18,14 @@ that way across source and compiler changes:
   before the settle that follows it;
 - and the kernels spill nothing.
 
+The fused backward's sweep kernel runs an item behind a call
+(fused_item_call): a call saves and restores the callee-saved registers
+through scratch, and the allocator copies a few of its own values.  For it
+the rule is the hazard itself: no compiler copy or scratch store reads a
+register that the function's assembly wrote last.  (The sweep kernel only
+takes tickets that no workgroup of their XCD took, which normally never
+happens; its speed does not matter.)
+
 Copies inside the kernels' own assembly blocks are deliberate and exempt.
 """
 import os
@@ -30,6 +38,8 @@ import pytest
 from exact_attention_bwd_amd import build as B
 
 KERNELS = (
+    ("attn_bwd.hip", "_ZN4attn3bwd16bwd_fused_kernel"),
+    ("attn_bwd.hip", "_ZN4attn3bwd15fused_item_call"),
     ("attn_bwd.hip", "_ZN4attn3bwd19bwd_dkdv_w64_kernelILb1E"),
     ("attn_bwd.hip", "_ZN4attn3bwd19bwd_dkdv_w64_kernelILb0E"),
     ("attn_bwd.hip", "_ZN4attn3bwd13bwd_dq_kernelILi128ELb1E"),
@@ -60,7 +70,7 @@ def isa(tmp_path_factory):
 
 
 def _body(lines, prefix):
-    start = next(i for i, l in enumerate(lines) if l.startswith(prefix) and l.split(":")[0].endswith("f"))
+    start = next(i for i, l in enumerate(lines) if l.startswith(prefix) and l.split(";")[0].rstrip().endswith(":"))
     end = next(i for i in range(start, len(lines)) if lines[i].startswith(".Lfunc_end"))
     return lines[start:end]
 
@@ -96,11 +106,24 @@ STORE = re.compile(r"^\s*(ds_write|buffer_store|global_store|flat_store|scratch_
 IMM = re.compile(r"^-?(0x[0-9a-f]+|\d+(\.\d+)?)$")
 
 
+FUNCTIONS = ("_ZN4attn3bwd15fused_item_call",)
+
+
 @pytest.mark.parametrize("src,kernel", KERNELS, ids=[k for _, k in KERNELS])
 def test_no_vector_register_copies(isa, src, kernel):
     body = _body(isa[src], kernel)
     assert any("v_mfma" in l for l in body), "kernel body not found"
-    mfma = [i for i, l in enumerate(body) if "v_mfma" in l]
+    # the products issued from assembly (their latency is unknown to the
+    # compiler); a kernel whose products are all compiler-issued: all of them
+    in_asm, asm_mfma = False, []
+    for i, l in enumerate(body):
+        if "ASMSTART" in l:
+            in_asm = True
+        elif "ASMEND" in l:
+            in_asm = False
+        elif in_asm and "v_mfma" in l:
+            asm_mfma.append(i)
+    mfma = asm_mfma or [i for i, l in enumerate(body) if "v_mfma" in l]
     first, last = mfma[0], mfma[-1]
     settle = next((i for i in range(last, len(body)) if "s_nop 15" in body[i]), len(body))
     # registers the kernels' own assembly writes (loads, products): the
@@ -120,6 +143,7 @@ def test_no_vector_register_copies(isa, src, kernel):
     bad = []
     inside = False
     const = set()          # registers whose latest value is an immediate (zero fills)
+    last_asm = {}          # register -> whether its latest writer (in program text) is assembly
     for i, l in enumerate(body):
         if "ASMSTART" in l:
             inside = True
@@ -127,6 +151,9 @@ def test_no_vector_register_copies(isa, src, kernel):
         if "ASMEND" in l:
             inside = False
             continue
+        if l.strip() and not STORE.match(l) and len(l.split(None, 1)) > 1:
+            for r in _regs(l.split(None, 1)[1].split(",")[0]):
+                last_asm[r] = inside
         if re.match(r"^\.LBB\S*:", l):
             const = set()                        # a block may be reached from elsewhere
             continue
@@ -146,8 +173,8 @@ def test_no_vector_register_copies(isa, src, kernel):
             continue                             # scalar source
         from_v = any(k == "v" for k, _ in srcs)
         if m.group(1).startswith("v_mov") or m.group(1) == "v_pk_mov_b32":
-            if from_v:
-                bad.append(l.strip())            # any copy of a VGPR
+            if from_v and (kernel not in FUNCTIONS or any(last_asm.get(r) for r in srcs)):
+                bad.append(l.strip())            # a copy of a VGPR (functions: whose latest writer is asm)
         elif first <= i < last and srcs & asm_dst:
             bad.append(l.strip())                # AGPR traffic among the products
         elif last <= i < settle and srcs & last_dst:
@@ -155,7 +182,35 @@ def test_no_vector_register_copies(isa, src, kernel):
     assert not bad, f"{kernel}: vector register copies {bad[:5]}"
 
 
-@pytest.mark.parametrize("src,kernel", KERNELS, ids=[k for _, k in KERNELS])
+@pytest.mark.parametrize("src,kernel", [k for k in KERNELS if k[1] in FUNCTIONS], ids=lambda k: str(k))
+def test_function_spills_are_not_of_pending_registers(isa, src, kernel):
+    body = _body(isa[src], kernel)
+    scratch = [i for i, l in enumerate(body) if "scratch_" in l]
+    # the callee-saved registers are saved before the first assembly block
+    # and restored after the last one; in between, no scratch store may
+    # write out a register whose latest writer (in program text) is the
+    # functions' assembly (its load or product may not have landed)
+    first = next(i for i, l in enumerate(body) if "ASMSTART" in l)
+    last = max(i for i, l in enumerate(body) if "ASMEND" in l)
+    last_asm, inside, bad = {}, False, []
+    for i, l in enumerate(body):
+        if "ASMSTART" in l:
+            inside = True
+            continue
+        if "ASMEND" in l:
+            inside = False
+            continue
+        parts = l.split(None, 1)
+        if "scratch_store" in l and first < i < last:
+            if any(last_asm.get(r) for r in _regs(parts[1].split(",")[1])):
+                bad.append(l.strip())
+        elif l.strip() and not STORE.match(l) and len(parts) > 1:
+            for r in _regs(parts[1].split(",")[0]):
+                last_asm[r] = inside
+    assert not bad, f"{kernel}: spills of registers the assembly wrote last {bad[:5]}"
+
+
+@pytest.mark.parametrize("src,kernel", [k for k in KERNELS if k[1] not in FUNCTIONS], ids=lambda k: str(k))
 def test_no_spills(isa, src, kernel):
     lines = isa[src]
     meta = next(i for i, l in enumerate(lines) if l.strip().startswith(".name:") and l.split()[-1].startswith(kernel))
@@ -163,3 +218,24 @@ def test_no_spills(isa, src, kernel):
     end = next((i for i in range(meta + 1, len(lines)) if lines[i].strip().startswith((".name:", "- .", "..."))), len(lines))
     spills = [int(l.split()[-1]) for l in lines[meta:end] if l.strip().startswith((".vgpr_spill_count:", ".sgpr_spill_count:"))]
     assert spills and max(spills) == 0, f"{kernel}: spills {spills}"
+
+
+@pytest.mark.parametrize("src,kernel", KERNELS, ids=[k for _, k in KERNELS])
+def test_no_scalar_loads_among_counted_lds_reads(isa, src, kernel):
+    """The kernels wait for their LDS reads with exact lgkmcnt counts, which
+    assume that only LDS reads are counted: a scalar memory load (also
+    counted by lgkmcnt, and completing out of order) between the first and
+    the last of those reads would make a wait end early."""
+    body = _body(isa[src], kernel)
+    inside, reads = False, []
+    for i, l in enumerate(body):
+        if "ASMSTART" in l:
+            inside = True
+        elif "ASMEND" in l:
+            inside = False
+        elif inside and l.strip().startswith("ds_read"):
+            reads.append(i)
+    assert reads, "no counted LDS reads found"
+    smem = [body[i].strip() for i in range(reads[0], reads[-1])
+            if body[i].strip().startswith(("s_load", "s_buffer_load", "s_scratch_load", "s_memtime", "s_memrealtime"))]
+    assert not smem, f"{kernel}: scalar loads among the counted LDS reads {smem[:3]}"

@@ -201,6 +201,36 @@ def test_caller_stream_is_used(lib):
         assert torch.equal(a[n], b[n]), n
 
 
+@pytest.mark.parametrize("B,H,N", [(1, 3, 333), (8, 16, 4096), (1, 1, 129)])
+def test_fused_control_block(lib, B, H, N):
+    """The causal d = 128 backward runs as one kernel whose work queues and
+    progress flags sit at the start of the workspace (then a one-workgroup
+    sweep kernel).  After a call: every item published its last query tile
+    (4 j for key tile j), no wait reached its bound, every workgroup checked
+    in, each queue's ticket counter ran one past its workgroups (the sweep's
+    last claim), and the sweep found nothing left (each XCD ran enough
+    workgroups for its queue)."""
+    import torch
+    cfg = DenseConfig("ctrl", B, H, N, 128, True, seed=21)
+    inp = make_dense_inputs(cfg)
+    q, k, v, do = (to_dev(inp[n]) for n in ("q", "k", "v", "do"))
+    o, lse = lib.attn_fwd(q, k, v, True, cfg.scale)
+    D = lib.attn_bwd_preprocess(o, do)
+    ws = torch.empty(lib.attn_bwd_workspace_bytes(B, H, N, 128, True), dtype=torch.uint8, device="cuda")
+    lib.attn_bwd(q, k, v, do, lse, D, True, cfg.scale, workspace=ws)
+    torch.cuda.synchronize()
+    tc2 = -(-N // 256)
+    nq0 = -(-(B * H) // 8)                      # heads of the largest queue, taken in pairs
+    per_xcd = (nq0 + 1) // 2 * 2 * tc2
+    ctrl = ws[: (64 + B * H * tc2) * 4].view(torch.int32).cpu().numpy()
+    say(f"  tickets {ctrl[:8].tolist()} finished {ctrl[8]} wait-bound {ctrl[9]} swept {ctrl[10]}")
+    assert ctrl[8] == 8 * per_xcd
+    assert ctrl[9] == 0 and ctrl[10] == 0
+    assert np.all(ctrl[:8] == per_xcd + 1)
+    prog = ctrl[64:].reshape(B * H, tc2)
+    assert np.array_equal(prog, np.tile(4 * np.arange(tc2), (B * H, 1))), prog
+
+
 # ----------------------------------------------------------------------------
 # Full-size workloads, in the launch configuration the benchmark times.  The
 # GPU path runs once per workload (cached); the tests below then compare its
