@@ -20,6 +20,7 @@ __all__ = [
     "attn_fwd", "attn_bwd_preprocess", "attn_bwd", "attn_bwd_workspace_bytes",
     "attn_fwd_gqa", "attn_bwd_gqa", "attn_bwd_gqa_workspace_bytes",
     "attention_backward", "attn_sparse_fwd", "attn_sparse_bwd", "attn_sparse_bwd_workspace_bytes",
+    "attn_bwd_noalloc", "attn_bwd_noalloc_max_workspace_bytes", "attn_bwd_workspace_bytes",
     "lib_path", "AttnError", "version",
 ]
 
@@ -69,6 +70,10 @@ def _load():
     lib.attn_sparse_bwd.restype = i
     lib.attn_sparse_bwd_timed.argtypes = [vp] * 12 + [sz, i, i, i, i, i, i, f, vp, vp, vp]
     lib.attn_sparse_bwd_timed.restype = i
+    lib.attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+    lib.attn_bwd_noalloc.restype = i
+    lib.attn_bwd_noalloc_max_workspace_bytes.argtypes = []
+    lib.attn_bwd_noalloc_max_workspace_bytes.restype = sz
     lib.attn_last_error.argtypes = []
     lib.attn_last_error.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -255,6 +260,29 @@ def attn_bwd_gqa(q, k, v, do, lse, D, causal: bool, scale: float | None = None,
     else:
         _check(_lib.attn_bwd_gqa_timed(*args, *(ctypes.c_void_p(e) for e in main_events)))
     return dq, dk, dv
+
+
+def attn_bwd_noalloc(q, k, v, do, lse, D, causal: bool, dq, dk, dv, scale: float | None = None,
+                     stream=None):
+    """attn_bwd with the library's static scratch as workspace: the C call
+    allocates nothing (the caller passes dq, dk, dv).  Shapes whose workspace
+    exceeds attn_bwd_noalloc_max_workspace_bytes() raise AttnError; calls that
+    overlap on one device race."""
+    shape = _shape4(q, "q")
+    for t, n in ((k, "k"), (v, "v"), (do, "dO"), (dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _same(shape, t, n)
+    B, H, N, d = shape
+    _stat(lse, (B, H, N), "lse")
+    _stat(D, (B, H, N), "D")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _check(_lib.attn_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(D), _ptr(dq), _ptr(dk),
+                                 _ptr(dv), B, H, N, d, int(bool(causal)), float(scale), _stream(stream)))
+    return dq, dk, dv
+
+
+def attn_bwd_noalloc_max_workspace_bytes() -> int:
+    return int(_lib.attn_bwd_noalloc_max_workspace_bytes())
 
 
 def attention_backward(q, k, v, do, o, lse, causal: bool, scale: float | None = None,

@@ -242,6 +242,29 @@ attn_status attn_sparse_bwd_timed(const void* q, const void* k, const void* v, c
                                   int dqk, int dv_dim, int topk, float scale, void* stream,
                                   void* main_start, void* main_stop);
 
+/*
+ * ---------------------------------------------------------------------------
+ * Backward without allocation, for callers that cannot allocate device
+ * memory (code under stream or graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): attn_bwd with its workspace in a static array of
+ * attn_bwd_noalloc_max_workspace_bytes() bytes (64 MiB) that the library
+ * holds on every device it runs on, until the process ends.  The array's
+ * device address is looked up on the first call on a device (a set-up step
+ * that allocates nothing); the call itself allocates and frees nothing.
+ * Shapes whose attn_bwd_workspace_bytes_ex(B, H, H, N, d, causal) exceeds that
+ * size are rejected with ATTN_ERR_WORKSPACE (e.g. causal d = 128 fits up to
+ * about three heads of N = 4096).  Every call on one device uses the same
+ * array: calls that overlap on a device (two streams, two threads) race and
+ * give wrong results; serialise them.  Arguments, results and other errors
+ * as attn_bwd.
+ */
+attn_status attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* dO,
+                             const float* lse, const float* D, void* dq, void* dk, void* dv, int B,
+                             int H, int N, int d, int causal, float scale, void* stream);
+
+/* Size in bytes of attn_bwd_noalloc's static scratch (the largest workspace it serves). */
+size_t attn_bwd_noalloc_max_workspace_bytes(void);
+
 /* Message describing the last non-OK status returned on this thread ("" if none). */
 const char* attn_last_error(void);
 
