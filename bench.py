@@ -250,11 +250,15 @@ SQ_PASS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIV
            "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "GRBM_GUI_ACTIVE"]
 
 
+HOST_ONLY_SOURCES = ("attn_api.hip", "attn_noalloc.hip", "api_error.hpp", "launch.hpp")
+
+
 def sources_sha():
-    """sha256 over every kernel source: a profile taken on other sources is stale."""
+    """sha256 over the device-code sources: a profile taken on other kernels
+    is stale (the host-side entry points do not count)."""
     h = hashlib.sha256()
     for p in sorted(glob.glob(os.path.join(CSRC, "*"))):
-        if p.endswith((".hip", ".hpp")):
+        if p.endswith((".hip", ".hpp")) and os.path.basename(p) not in HOST_ONLY_SOURCES:
             with open(p, "rb") as f:
                 h.update(os.path.basename(p).encode())
                 h.update(f.read())
