@@ -19,12 +19,18 @@
 //    and K chunks that are read with a transposing LDS read are copied into
 //    LDS by per-lane-addressed buffer -> LDS copies, i.e. the gather itself.
 //  * dK and dV: the PR adds every row's contribution into fp32 buffers with
-//    atomics.  fp32 atomics on this GPU run at about 1.3 TB/s wherever the
-//    target lives, and C5 needs 9.1 GB of them.  Instead the per-row kernel
-//    stores each (row, slot)'s contribution (summed over the head group) with
-//    plain stores, a counting-sort transpose of the index lists gives every
-//    key its list of (row, slot) pairs in row order, and a reduction kernel
-//    sums them per key in that fixed order.
+//    atomics.  fp32 atomics on this GPU run at about 1.3 TB/s of payload
+//    wherever the target lives (in or out of L2, any scope), and a 4096-row,
+//    top-512 problem needs 9.1 GB of them.  Instead the per-row kernel stores
+//    each (row, slot)'s contribution (summed over the head group) with plain
+//    stores, a counting-sort transpose of the index lists gives every key its
+//    list of (row, slot) pairs in row order, and a reduction kernel sums them
+//    per key in that fixed order, in fp32.
+//  * a stored contribution is fp16 times a power of two chosen per (row, slot)
+//    and per part (dV, dK) from a bound on its magnitude, so it cannot
+//    overflow and keeps fp16's 11-bit significand: a relative error of at most
+//    2^-12 per stored value, 8x below the bf16 rounding of the output, at half
+//    the bytes of fp32.
 //  * dQ = scale * dS K_I needs dS with one head per lane, so the per-row
 //    kernel stores dS (bf16, as the PR rounds it for its dQ product) and a
 //    second per-row kernel forms dQ in registers, as in the dense backward.
@@ -39,7 +45,7 @@ constexpr int DV = 512;
 constexpr int HG = 64;                 // query heads per workgroup
 constexpr int QROW = 1280;             // LDS row stride (bytes) of a 576-wide bf16 row
 constexpr int VROW = 1024;             // LDS row stride (bytes) of a 512-wide bf16 row
-constexpr int PW = DV + DQK;           // fp32 words of one (row, slot) dK/dV contribution
+constexpr int PW = DV + DQK;           // fp16 values of one (row, slot) dK/dV contribution
 constexpr int RB = 16;                 // query rows per block of the index transpose
 constexpr int MAX_NKV = 16384;         // keys the transpose can count in LDS
 constexpr int SBW_WAVES = 8;           // waves of the per-row backward kernel
@@ -261,7 +267,8 @@ void sfwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 // ----------------------------------------------------------------------------
 // Backward, per (query row, head group): recompute S = Q_i K_I^T, P, dP =
 // dO_i V_I^T and dS; store dS (bf16) for the dQ kernel and each slot's dV and
-// (unscaled) dK contribution, summed over the 64 heads, as fp32.  Eight waves
+// (unscaled) dK contribution, summed over the 64 heads, as scaled fp16 (the
+// two powers of two go to `pscale`, see contrib_exp).  Eight waves
 // (two per SIMD); wave w owns slots 32 w .. + 31 of every 256-slot chunk and
 // all 64 heads: S and dP have
 // one slot per lane, which is the A layout of P^T and dS^T for dV = P^T dO and
@@ -273,16 +280,30 @@ struct BwdSmem {
     static constexpr int off_do = off_q + HG * QROW;         // 64 x VROW
     static constexpr int off_l = off_do + HG * VROW;         // 64 floats (L log2 e)
     static constexpr int off_d = off_l + HG * 4;             // 64 floats (D)
-    static constexpr int bytes = off_d + HG * 4;
+    static constexpr int off_mq = off_d + HG * 4;            // 64 floats: max |Q_h,:|
+    static constexpr int off_mdo = off_mq + HG * 4;          // 64 floats: max |dO_h,:|
+    static constexpr int off_sc = off_mdo + HG * 4;          // per wave: [2][32] inverse scales
+    static constexpr int bytes = off_sc + SBW_WAVES * 2 * 32 * 4;
 };
+
+// Power-of-two scale of a stored contribution whose entries are at most `b`
+// in magnitude: the stored value is c * 2^-e in fp16 with 2^-e b <= 2^14, so
+// it stays below fp16's largest finite value with a factor 4 to spare (enough
+// for the bf16 rounding of P and dS and the fp32 sums behind c); e is kept
+// >= -120 so that 2^e and 2^-e are normal floats.
+__device__ __forceinline__ int contrib_exp(float b) {
+    const int e = __builtin_amdgcn_frexp_expf(b) - 14;     // b < 2^(e + 14) for b > 0
+    return e < -120 ? -120 : e;
+}
 
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void sbwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                       const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                       const float* __restrict__ Lse, const float* __restrict__ Dd,
                       const int* __restrict__ idx, const int* __restrict__ tlen,
-                      __bf16* __restrict__ dsw, float* __restrict__ part, int Hq, int Nq, int Nkv,
-                      int topk, int tpad, float scale) {
+                      __bf16* __restrict__ dsw, _Float16* __restrict__ part,
+                      float2* __restrict__ pscale, int Hq, int Nq, int Nkv, int topk, int tpad,
+                      float scale) {
     using S = BwdSmem;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int lane = threadIdx.x & 63, w = wave_id();
@@ -309,11 +330,43 @@ void sbwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
         reinterpret_cast<float*>(smem + S::off_d)[lane] = Dd[hrow];
     }
     __syncthreads();
+    // ---- max |Q_h,:| and max |dO_h,:| per head: 8 lanes per head, 9 (Q) and 8
+    //      (dO) 16-byte chunks per lane, then a max over the 8 lanes
+    {
+        const int h = threadIdx.x >> 3, p = threadIdx.x & 7;
+        auto chunk_max = [](const char* row, int c, float m) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(row + c * 16);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                m = fmaxf(m, fabsf(__uint_as_float(v[e] << 16)));
+                m = fmaxf(m, fabsf(__uint_as_float(v[e] & 0xffff0000u)));
+            }
+            return m;
+        };
+        float mq = 0.f, md = 0.f;
+#pragma unroll
+        for (int m = 0; m < DQK / 64; ++m) mq = chunk_max(smem + S::off_q + h * QROW, lchunk(h, p + 8 * m), mq);
+#pragma unroll
+        for (int m = 0; m < DV / 64; ++m) md = chunk_max(smem + S::off_do + h * VROW, lchunk(h, p + 8 * m), md);
+#pragma unroll
+        for (int x = 1; x < 8; x <<= 1) {
+            mq = fmaxf(mq, __shfl_xor(mq, x));
+            md = fmaxf(md, __shfl_xor(md, x));
+        }
+        if (p == 0) {
+            reinterpret_cast<float*>(smem + S::off_mq)[h] = mq;
+            reinterpret_cast<float*>(smem + S::off_mdo)[h] = md;
+        }
+    }
+    __syncthreads();
 
     const __bf16* Qs = reinterpret_cast<const __bf16*>(smem + S::off_q);
     const __bf16* dOs = reinterpret_cast<const __bf16*>(smem + S::off_do);
     const float* Ls = reinterpret_cast<const float*>(smem + S::off_l);
     const float* Ds = reinterpret_cast<const float*>(smem + S::off_d);
+    const float* MQs = reinterpret_cast<const float*>(smem + S::off_mq);
+    const float* MDs = reinterpret_cast<const float*>(smem + S::off_mdo);
+    float* scw = reinterpret_cast<float*>(smem + S::off_sc) + w * 64;   // [0..31] dV, [32..63] dK
     const char* Qb = smem + S::off_q;
     const char* dOb = smem + S::off_do;
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(K, Nkv * DQK * 2);
@@ -376,9 +429,11 @@ void sbwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
 #pragma unroll
             for (int e = 0; e < GK; ++e) gcur[e] = gnext[e];
         }
-        // ---- P = exp(scale S - L) (0 for absent slots), dS = P (dP - D)
+        // ---- P = exp(scale S - L) (0 for absent slots), dS = P (dP - D); the
+        //      slot's bounds sum_h |P| max|dO_h| and sum_h |dS| max|Q_h|
         const bool live = key >= 0;
         bf16x8 pa[2][2], da[2][2];
+        float bv = 0.f, bk = 0.f;
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb) {
 #pragma unroll
@@ -386,6 +441,8 @@ void sbwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
                 const int h0 = hb * 32 + 8 * q + 4 * g;
                 const f32x4 lv = *reinterpret_cast<const f32x4*>(Ls + h0);
                 const f32x4 dd = *reinterpret_cast<const f32x4*>(Ds + h0);
+                const f32x4 mq = *reinterpret_cast<const f32x4*>(MQs + h0);
+                const f32x4 md = *reinterpret_cast<const f32x4*>(MDs + h0);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = q * 4 + e;
@@ -394,6 +451,8 @@ void sbwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
                                          : 0.f;
                     sc[hb][r] = p;
                     dp[hb][r] = p * (dp[hb][r] - dd[e]);
+                    bv = __builtin_fmaf(p, md[e], bv);
+                    bk = __builtin_fmaf(fabsf(dp[hb][r]), mq[e], bk);
                 }
             }
             pa[hb][0] = pack_c8(sc[hb], 0);
@@ -415,10 +474,38 @@ void sbwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
                     *reinterpret_cast<bf16x4*>(drow + dsoff(slot, u)) = __builtin_convertvector(v, bf16x4);
                 }
         }
-        // ---- dV and dK contributions of the 32 slots, 4 column blocks at a time:
-        //      C[m = slot][n = column], k = the 64 heads
-        float* prow = part + (rowg * topk) * PW;
+        // ---- the slot's scales: the two lane halves hold the heads' halves of
+        //      the bounds; inverse scales to LDS for the store layout below,
+        //      the scales themselves to pscale for the reduction
         const int slot0 = c * SBW_CHUNK + w * 32;
+        {
+            bv += __shfl_xor(bv, 32);
+            bk += __shfl_xor(bk, 32);
+            const int ev = contrib_exp(bv), ek = contrib_exp(bk);
+            if (g == 0) {
+                scw[l32] = __builtin_amdgcn_ldexpf(1.f, -ev);
+                scw[32 + l32] = __builtin_amdgcn_ldexpf(1.f, -ek);
+                if (live)
+                    pscale[rowg * topk + slot] =
+                        make_float2(__builtin_amdgcn_ldexpf(1.f, ev), __builtin_amdgcn_ldexpf(1.f, ek));
+            }
+            // the reads below are this wave's own LDS writes: LDS requests of a
+            // wave complete in order, so waiting for the writes suffices
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            __builtin_amdgcn_wave_barrier();
+        }
+        // ---- dV and dK contributions of the 32 slots, 4 column blocks at a time:
+        //      C[m = slot][n = column], k = the 64 heads.  Register r of half g
+        //      holds slot 8 (r >> 2) + 4 g + (r & 3) at column l32; lanes 2m and
+        //      2m + 1 swap one value of each register pair (r, r + 1) so that
+        //      each lane stores two adjacent fp16 columns of one slot.
+        _Float16* prow = part + (rowg * topk) * PW;
+        f32x4 isc[4];                            // inverse scales of this lane's 16 slots
+        auto load_isc = [&](int part_off) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) isc[q] = *reinterpret_cast<const f32x4*>(scw + part_off + 8 * q + 4 * g);
+        };
+        const int odd = l32 & 1;
         auto contrib = [&](const char* tile, int stride, bool is_v, int nblk, int blk0, int colbase) {
             f32x16 cacc[2];
 #pragma unroll
@@ -444,16 +531,27 @@ void sbwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
             for (int b = 0; b < 2; ++b) {
                 if (b < nblk) {
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int sl = 8 * (r >> 2) + 4 * g + (r & 3);
+                    for (int r = 0; r < 16; r += 2) {
+                        const uint32_t h0 = __builtin_bit_cast(
+                            uint16_t, (_Float16)(cacc[b][r] * isc[r >> 2][r & 3]));
+                        const uint32_t h1 = __builtin_bit_cast(
+                            uint16_t, (_Float16)(cacc[b][r + 1] * isc[r >> 2][(r & 3) + 1]));
+                        // quad_perm [1, 0, 3, 2]: the value of lane l ^ 1
+                        const uint32_t got = (uint32_t)__builtin_amdgcn_mov_dpp(
+                            (int)(odd ? h0 : h1), 0xb1, 0xf, 0xf, false);
+                        const uint32_t word = odd ? (got | (h1 << 16)) : (h0 | (got << 16));
+                        const int sl = 8 * (r >> 2) + 4 * g + (r & 3) + odd;
                         if ((vmask >> sl) & 1)
-                            prow[(size_t)(slot0 + sl) * PW + colbase + 32 * (blk0 + b) + l32] = cacc[b][r];
+                            *reinterpret_cast<uint32_t*>(
+                                prow + (size_t)(slot0 + sl) * PW + colbase + 32 * (blk0 + b) + l32 - odd) = word;
                     }
                 }
             }
         };
+        load_isc(0);
 #pragma unroll 1
         for (int blk = 0; blk < DV / 32; blk += 2) contrib(dOb, VROW, true, 2, blk, 0);
+        load_isc(32);
 #pragma unroll 1
         for (int blk = 0; blk < DQK / 32; blk += 2) contrib(Qb, QROW, false, 2, blk, DV);
     }
@@ -655,87 +753,86 @@ __global__ __launch_bounds__(256) void sidx_fill_kernel(const int* __restrict__ 
 // sums are added in segment order, so that the result does not depend on
 // timing.  (A key can collect thousands of rows, the first keys of a causal
 // selection most of all; one wave per key left those few keys to set the
-// kernel's length.)  Lane l sums the 16-byte chunks l, l + 64, l + 128,
-// l + 192 of each 4352-byte contribution row and word 1024 + l; rows are
-// loaded four at a time so that 20 loads per lane are in flight.
+// kernel's length.)  A contribution row is 2176 bytes of fp16: lane l takes
+// the 16-byte chunks l (dV columns 8l ..) and 64 + l (dK columns 8l ..) and
+// the value 1024 + l (dK column 512 + l), multiplies them by the row's
+// power-of-two scales (exact) and adds in fp32; rows are loaded four at a
+// time so that 12 loads per lane are in flight.
 constexpr int RW = 4;                            // waves per key
 
-__global__ __launch_bounds__(RW * 64) void sbwd_reduce_kernel(const float* __restrict__ part,
+__global__ __launch_bounds__(RW * 64) void sbwd_reduce_kernel(const _Float16* __restrict__ part,
+                                                             const float2* __restrict__ pscale,
                                                              const int* __restrict__ off,
                                                              const int* __restrict__ list,
                                                              __bf16* __restrict__ dK,
                                                              __bf16* __restrict__ dV, int Nkv, int G,
                                                              int topk, float scale) {
-    static_assert(PW == 4 * 256 + 64, "row layout: four 1 KiB chunks per 64 lanes and 64 words");
-    __shared__ f32x4 red4[RW - 1][4][64];
+    static_assert(PW == 2 * 512 + 64, "row layout: two 1 KiB chunks per 64 lanes and 64 values");
+    typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+    typedef float f32x8 __attribute__((ext_vector_type(8)));
+    __shared__ f32x8 red8[RW - 1][2][64];
     __shared__ float redt[RW - 1][64];
     const int lane = threadIdx.x & 63;
     const int w = wave_id();
     const int j = blockIdx.x;
-    f32x4 acc[4];
-    float acct = 0.f;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x8 av = {}, ak = {};
+    float at = 0.f;
     // contribution rows of key j: (list entry e, head group hg), e in list order
     const int e0 = off[j];
     const int nrows = (off[j + 1] - e0) * G;
-    auto row_of = [&](int r) -> const float* {
+    auto row_of = [&](int r) -> size_t {
         const int pr = list[e0 + r / G];          // i * topk + s
         const int i = pr / topk, s = pr - i * topk;
-        return part + (((size_t)i * G + r % G) * topk + s) * PW;
+        return ((size_t)i * G + r % G) * topk + s;
+    };
+    auto add_row = [&](f16x8 v, f16x8 k, _Float16 t, float2 m) {
+        av += __builtin_convertvector(v, f32x8) * m.x;
+        ak += __builtin_convertvector(k, f32x8) * m.y;
+        at += (float)t * m.y;
     };
     // this wave's segment [r0, r1)
     const int r0 = (int)((long long)nrows * w / RW), r1 = (int)((long long)nrows * (w + 1) / RW);
     int r = r0;
     for (; r + 4 <= r1; r += 4) {
-        f32x4 v[4][4];
-        float t[4];
+        f16x8 v[4], k[4];
+        _Float16 t[4];
+        float2 m[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const float* row = row_of(r + u);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) v[u][c] = reinterpret_cast<const f32x4*>(row)[c * 64 + lane];
+            const size_t pr = row_of(r + u);
+            const _Float16* row = part + pr * PW;
+            v[u] = reinterpret_cast<const f16x8*>(row)[lane];
+            k[u] = reinterpret_cast<const f16x8*>(row)[64 + lane];
             t[u] = row[1024 + lane];
+            m[u] = pscale[pr];
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) acc[c] += v[u][c];
-            acct += t[u];
-        }
+        for (int u = 0; u < 4; ++u) add_row(v[u], k[u], t[u], m[u]);
     }
     for (; r < r1; ++r) {
-        const float* row = row_of(r);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[c] += reinterpret_cast<const f32x4*>(row)[c * 64 + lane];
-        acct += row[1024 + lane];
+        const size_t pr = row_of(r);
+        const _Float16* row = part + pr * PW;
+        add_row(reinterpret_cast<const f16x8*>(row)[lane], reinterpret_cast<const f16x8*>(row)[64 + lane],
+                row[1024 + lane], pscale[pr]);
     }
     // segment sums 1 .. RW-1 to wave 0, added in segment order
     if (w > 0) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) red4[w - 1][c][lane] = acc[c];
-        redt[w - 1][lane] = acct;
+        red8[w - 1][0][lane] = av;
+        red8[w - 1][1][lane] = ak;
+        redt[w - 1][lane] = at;
     }
     __syncthreads();
     if (w != 0) return;
 #pragma unroll
     for (int q = 0; q < RW - 1; ++q) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[c] += red4[q][c][lane];
-        acct += redt[q][lane];
+        av += red8[q][0][lane];
+        ak += red8[q][1][lane];
+        at += redt[q][lane];
     }
-    // columns 4 lane + 256 c (+0..3): c = 0, 1 are dV, c = 2, 3 and 1024 + lane are dK
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const int col = 4 * lane + 256 * c;
-        if (c < 2) {
-            *reinterpret_cast<bf16x4*>(dV + (size_t)j * DV + col) = __builtin_convertvector(acc[c], bf16x4);
-        } else {
-            *reinterpret_cast<bf16x4*>(dK + (size_t)j * DQK + col - DV) =
-                __builtin_convertvector(acc[c] * scale, bf16x4);
-        }
-    }
-    dK[(size_t)j * DQK + 1024 + lane - DV] = (__bf16)(acct * scale);
+    typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+    *reinterpret_cast<bf16x8v*>(dV + (size_t)j * DV + 8 * lane) = __builtin_convertvector(av, bf16x8v);
+    *reinterpret_cast<bf16x8v*>(dK + (size_t)j * DQK + 8 * lane) = __builtin_convertvector(ak * scale, bf16x8v);
+    dK[(size_t)j * DQK + 512 + lane] = (__bf16)(at * scale);
 }
 
 }  // namespace sp
@@ -748,15 +845,16 @@ static int sp_tpad(int topk) { return ((topk + sp::SBW_CHUNK - 1) / sp::SBW_CHUN
 static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace: [block counts nb x Nkv int32][off Nkv + 1 int32][pair list
-// Nq x topk int32][dS^T Nq x G x tpad x 64 bf16][contributions Nq x G x topk
-// x 1088 fp32], each segment 256-byte aligned.  Nothing needs initialising:
-// every word read is written earlier in the same call.
+// Nq x topk int32][dS^T Nq x G x tpad x 64 bf16][contribution scales Nq x G x
+// topk float2][contributions Nq x G x topk x 1088 fp16], each segment
+// 256-byte aligned.  Nothing needs initialising: every word read is written
+// earlier in the same call.
 size_t sparse_bwd_workspace_bytes(int Hq, int Nq, int Nkv, int topk) {
     const size_t G = (size_t)Hq / sp::HG;
     const size_t nb = ((size_t)Nq + sp::RB - 1) / sp::RB;
     return al256(nb * Nkv * 4) + al256(((size_t)Nkv + 1) * 4) + al256((size_t)Nq * topk * 4) +
-           al256((size_t)Nq * G * sp_tpad(topk) * sp::HG * 2) +
-           al256((size_t)Nq * G * topk * sp::PW * 4);
+           al256((size_t)Nq * G * sp_tpad(topk) * sp::HG * 2) + al256((size_t)Nq * G * topk * 8) +
+           al256((size_t)Nq * G * topk * sp::PW * 2);
 }
 
 hipError_t launch_sparse_fwd(const void* q, const void* k, const void* v, const int* idx,
@@ -792,7 +890,9 @@ hipError_t launch_sparse_bwd(const void* q, const void* k, const void* v, const 
     ws += al256((size_t)Nq * topk * 4);
     __bf16* dsw = (__bf16*)ws;
     ws += al256((size_t)Nq * G * tpad * sp::HG * 2);
-    float* part = (float*)ws;
+    float2* pscale = (float2*)ws;
+    ws += al256((size_t)Nq * G * topk * 8);
+    _Float16* part = (_Float16*)ws;
 
     hipError_t e;
     if (nb > 0) {
@@ -824,7 +924,7 @@ hipError_t launch_sparse_bwd(const void* q, const void* k, const void* v, const 
         if (main_start && (e = hipEventRecord(main_start, stream)) != hipSuccess) return e;
         hipLaunchKernelGGL(sp::sbwd_main_kernel, dim3(Nq * G), dim3(sp::SBW_WAVES * 64), smem_main, stream,
                            (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dO,
-                           lse, D, idx, tlen, dsw, part, Hq, Nq, Nkv, topk, tpad, scale);
+                           lse, D, idx, tlen, dsw, part, pscale, Hq, Nq, Nkv, topk, tpad, scale);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (main_stop && (e = hipEventRecord(main_stop, stream)) != hipSuccess) return e;
         hipLaunchKernelGGL(sp::sbwd_dq_kernel, dim3(Nq * G), dim3(256), smem_dq, stream,
@@ -834,7 +934,7 @@ hipError_t launch_sparse_bwd(const void* q, const void* k, const void* v, const 
     }
     if (Nkv > 0) {
         hipLaunchKernelGGL(sp::sbwd_reduce_kernel, dim3(Nkv), dim3(sp::RW * 64), 0, stream, part,
-                           off, list, (__bf16*)dk, (__bf16*)dv, Nkv, G, topk, scale);
+                           pscale, off, list, (__bf16*)dk, (__bf16*)dv, Nkv, G, topk, scale);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     return hipSuccess;

@@ -206,10 +206,11 @@ attn_status attn_sparse_fwd(const void* q, const void* k, const void* v, const i
 /*
  * Workspace of attn_sparse_bwd: a per-row-block key histogram
  * (ceil(Nq/16) x Nkv int32), key offsets (Nkv + 1 int32), the transposed pair
- * list (Nq x topk int32), dS (Nq x Hq/64 x ceil(topk/256)*256 x 64 bf16) and
- * each (row, head group, slot)'s dK/dV contribution (Nq x Hq/64 x topk x 1088
- * fp32; 9.1 GB at Hq = 64, Nq = 4096, topk = 512), each 256-byte aligned.
- * 0 for unsupported or empty problems.
+ * list (Nq x topk int32), dS (Nq x Hq/64 x ceil(topk/256)*256 x 64 bf16), the
+ * two power-of-two scales of each (row, head group, slot) (float2) and its
+ * dK/dV contribution (Nq x Hq/64 x topk x 1088 fp16; 4.6 GB at Hq = 64,
+ * Nq = 4096, topk = 512), each 256-byte aligned.  0 for unsupported or empty
+ * problems.
  */
 size_t attn_sparse_bwd_workspace_bytes(int Hq, int Nq, int Nkv, int dqk, int dv, int topk);
 
@@ -219,10 +220,13 @@ size_t attn_sparse_bwd_workspace_bytes(int Hq, int Nq, int Nkv, int dqk, int dv,
  * (every key row, zero for keys no row selected).  Kernels, all on `stream`:
  * a counting-sort transpose of the index lists (per key, its (row, slot)
  * pairs in row order), a per-row kernel that recomputes S, P, dP, dS for the
- * 64 heads of a group and stores dS and each slot's dK/dV contribution, a
- * per-row dQ kernel, and a per-key reduction of the contributions in that
- * fixed order.  No floating-point atomics: results are reproducible, except
- * that a key repeated within one row's list is summed in an unspecified order.
+ * 64 heads of a group and stores dS and each slot's dK/dV contribution (fp16
+ * times a power of two bounded from the slot's P, dS and the row's max |Q|,
+ * |dO|, so a stored value carries a relative error of at most 2^-12), a
+ * per-row dQ kernel, and a per-key fp32 reduction of the contributions in
+ * that fixed order.  No floating-point atomics: results are reproducible,
+ * except that a key repeated within one row's list is summed in an
+ * unspecified order.
  */
 attn_status attn_sparse_bwd(const void* q, const void* k, const void* v, const void* dO,
                             const float* lse, const float* D, const int* idx, const int* topk_len,

@@ -148,14 +148,15 @@ def test_sparse_validation_errors_do_not_launch(ea):
 
 def test_sparse_workspace_size(ea):
     # per-row-block key counts, key offsets, pair list, dS (64 heads per slot,
-    # slots padded to 256) and the fp32 dK/dV contribution of every slot
+    # slots padded to 256), the two fp32 scales and the fp16 dK/dV contribution
+    # of every slot
     al = lambda x: (x + 255) // 256 * 256  # noqa: E731
     got = ea.attn_sparse_bwd_workspace_bytes(64, 4096, 4096, 512)
     assert got == (al(256 * 4096 * 4) + al(4097 * 4) + al(4096 * 512 * 4) + al(4096 * 512 * 64 * 2)
-                   + al(4096 * 512 * 1088 * 4))
+                   + al(4096 * 512 * 8) + al(4096 * 512 * 1088 * 2))
     assert ea.attn_sparse_bwd_workspace_bytes(128, 300, 280, 100) == (
         al(19 * 280 * 4) + al(281 * 4) + al(300 * 100 * 4) + al(300 * 2 * 256 * 64 * 2)
-        + al(300 * 2 * 100 * 1088 * 4))
+        + al(300 * 2 * 100 * 8) + al(300 * 2 * 100 * 1088 * 2))
     assert ea.attn_sparse_bwd_workspace_bytes(0, 0, 0, 8) == 0
 
 
