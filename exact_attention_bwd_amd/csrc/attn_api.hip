@@ -195,6 +195,7 @@ attn_status check_sparse(int Hq, int Nq, int Nkv, int dqk, int dv, int topk, boo
     if (Hq % 64 != 0) return fail(ATTN_ERR_UNSUPPORTED, "Hq=%d is not a multiple of 64", Hq);
     if (Nkv > (1 << 20)) return fail(ATTN_ERR_UNSUPPORTED, "Nkv=%d above 1048576", Nkv);
     if (bwd && Nkv > 16384) return fail(ATTN_ERR_UNSUPPORTED, "sparse backward: Nkv=%d above 16384", Nkv);
+    if (bwd && topk > 65536) return fail(ATTN_ERR_UNSUPPORTED, "sparse backward: topk=%d above 65536", topk);
     if ((long long)Nq * topk > 0x7fffffffLL || (long long)Nq * (Hq / 64) > 0x7fffffffLL)
         return fail(ATTN_ERR_UNSUPPORTED, "sizes too large Nq=%d topk=%d Hq=%d", Nq, topk, Hq);
     return ATTN_OK;

@@ -50,6 +50,9 @@ constexpr int RB = 16;                 // query rows per block of the index tran
 constexpr int MAX_NKV = 16384;         // keys the transpose can count in LDS
 constexpr int SBW_WAVES = 8;           // waves of the per-row backward kernel
 constexpr int SBW_CHUNK = SBW_WAVES * 32;   // slots per chunk of that kernel
+constexpr int kDropOffset = 0x40000000;    // buffer offset past any contribution block
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // LDS rows start on a 256-byte bank line; the 16-byte chunk c of row r is
 // stored at chunk (c & ~15) | ((c & 15) ^ lswz(r)).  For any 16 consecutive
@@ -374,6 +377,11 @@ void sbwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
     const float sl2 = scale * kLog2e;
     (void)Qs;
     (void)dOs;
+    // this row's contribution block, and the v_perm selector that keeps
+    // (own low, partner's low) on even lanes, (partner's high, own high) on odd
+    const __amdgpu_buffer_rsrc_t prs = make_rsrc(part + rowg * topk * PW, topk * PW * 2);
+    const int odd = l32 & 1;
+    const uint32_t psel = odd ? 0x03020706u : 0x05040100u;
 
     for (int c = 0; c < nchunks; ++c) {
         const int slot = c * SBW_CHUNK + w * 32 + l32;            // this lane's slot
@@ -498,14 +506,24 @@ void sbwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
         //      C[m = slot][n = column], k = the 64 heads.  Register r of half g
         //      holds slot 8 (r >> 2) + 4 g + (r & 3) at column l32; lanes 2m and
         //      2m + 1 swap one value of each register pair (r, r + 1) so that
-        //      each lane stores two adjacent fp16 columns of one slot.
-        _Float16* prow = part + (rowg * topk) * PW;
+        //      each lane stores two adjacent fp16 columns of one slot: the even
+        //      lane slot 8 (r >> 2) + 4 g + (r & 3), the odd lane the next one.
+        //      Stores go through a descriptor over this row's block with
+        //      per-lane byte offsets fixed for the chunk; absent slots get an
+        //      offset past the block's end, so their stores are dropped.
         f32x4 isc[4];                            // inverse scales of this lane's 16 slots
         auto load_isc = [&](int part_off) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) isc[q] = *reinterpret_cast<const f32x4*>(scw + part_off + 8 * q + 4 * g);
         };
-        const int odd = l32 & 1;
+        int voff[4][2];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) {
+                const int sl = 8 * q + 2 * pp + 4 * g + odd;
+                voff[q][pp] = ((vmask >> sl) & 1) ? (slot0 + sl) * (PW * 2) + 2 * (l32 - odd) : kDropOffset;
+            }
         auto contrib = [&](const char* tile, int stride, bool is_v, int nblk, int blk0, int colbase) {
             f32x16 cacc[2];
 #pragma unroll
@@ -527,23 +545,19 @@ void sbwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
                         }
                     }
                 }
+            const int coff = 2 * (colbase + 32 * blk0);       // uniform byte offset of the column block
 #pragma unroll
             for (int b = 0; b < 2; ++b) {
                 if (b < nblk) {
 #pragma unroll
                     for (int r = 0; r < 16; r += 2) {
-                        const uint32_t h0 = __builtin_bit_cast(
-                            uint16_t, (_Float16)(cacc[b][r] * isc[r >> 2][r & 3]));
-                        const uint32_t h1 = __builtin_bit_cast(
-                            uint16_t, (_Float16)(cacc[b][r + 1] * isc[r >> 2][(r & 3) + 1]));
-                        // quad_perm [1, 0, 3, 2]: the value of lane l ^ 1
-                        const uint32_t got = (uint32_t)__builtin_amdgcn_mov_dpp(
-                            (int)(odd ? h0 : h1), 0xb1, 0xf, 0xf, false);
-                        const uint32_t word = odd ? (got | (h1 << 16)) : (h0 | (got << 16));
-                        const int sl = 8 * (r >> 2) + 4 * g + (r & 3) + odd;
-                        if ((vmask >> sl) & 1)
-                            *reinterpret_cast<uint32_t*>(
-                                prow + (size_t)(slot0 + sl) * PW + colbase + 32 * (blk0 + b) + l32 - odd) = word;
+                        // x = (slot r, slot r + 1) at this lane's column; y = the same of lane l ^ 1
+                        const f16x2 hx = __builtin_convertvector(
+                            (f32x2{cacc[b][r] * isc[r >> 2][r & 3], cacc[b][r + 1] * isc[r >> 2][(r & 3) + 1]}), f16x2);
+                        const uint32_t x = __builtin_bit_cast(uint32_t, hx);
+                        const uint32_t y = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xb1, 0xf, 0xf, false);
+                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_amdgcn_perm(y, x, psel), prs,
+                                                              voff[r >> 2][(r & 3) >> 1] + 64 * b, coff, 0);
                     }
                 }
             }

@@ -196,8 +196,8 @@ attn_status attn_bwd_gqa_timed(const void* q, const void* k, const void* v, cons
  * slots (e.g. -1 padding) are ignored.  A row with no valid slot gets O = 0,
  * L = -inf and zero gradients.  Supported: dqk = 576, dv = 512, Hq a multiple
  * of 64 (heads are processed in groups of 64 that share each gathered K/V
- * row), Nkv <= 1048576 (backward: Nkv <= 16384).  Pointer alignment as for the
- * dense calls; idx and topk_len 4-byte aligned.
+ * row), Nkv <= 1048576 (backward: Nkv <= 16384, topk <= 65536).  Pointer
+ * alignment as for the dense calls; idx and topk_len 4-byte aligned.
  */
 attn_status attn_sparse_fwd(const void* q, const void* k, const void* v, const int* idx,
                             const int* topk_len, void* o, float* lse, int Hq, int Nq, int Nkv,

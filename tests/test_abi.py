@@ -144,6 +144,11 @@ def test_sparse_validation_errors_do_not_launch(ea):
                                f(0.1), None) == -4
     assert lib.attn_sparse_bwd(p, p, p, p, p, p, p, None, p, p, p, p, 1 << 40, 64, 16, 20000, 576, 512, 8,
                                f(0.1), None) == -2
+    # backward top-k limit: a row's contribution block must stay far below 1 GiB
+    assert lib.attn_sparse_bwd_workspace_bytes(64, 16, 16, 576, 512, 65537) == 0
+    assert lib.attn_sparse_bwd(p, p, p, p, p, p, p, None, p, p, p, p, 1 << 40, 64, 16, 16, 576, 512, 65537,
+                               f(0.1), None) == -2
+    assert b"topk" in lib.attn_last_error()
 
 
 def test_sparse_workspace_size(ea):
