@@ -34,6 +34,7 @@
 //  * dQ = scale * dS K_I needs dS with one head per lane, so the per-row
 //    kernel stores dS (bf16, as the PR rounds it for its dQ product) and a
 //    second per-row kernel forms dQ in registers, as in the dense backward.
+#include "asm_ops.hpp"
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -397,26 +398,29 @@ void sbwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
             sc[hb] = zero16();
             dp[hb] = zero16();
         }
-        // gathered K / V operands in groups of 4 k steps, one group in flight
+        // gathered K / V operands in groups of 4 k steps, two groups in flight
         // ahead of the products (the sched barriers keep the compiler from
         // hoisting all 68 loads)
-        constexpr int GK = 4;
+        constexpr int GK = 4, PF = 2;
         auto gload = [&](__amdgpu_buffer_rsrc_t rs, int base, int ks) {
             return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, base + 32 * ks, 0, 0));
         };
-        bf16x8 gcur[GK], gnext[GK];
+        constexpr int NG = (DQK + DV) / 16 / GK;
+        bf16x8 gb[PF + 1][GK];
+        auto gissue = [&](int grp, bf16x8* dst) {
 #pragma unroll
-        for (int e = 0; e < GK; ++e) gcur[e] = gload(krs, kbq, e);
-#pragma unroll
-        for (int grp = 0; grp < (DQK + DV) / 16 / GK; ++grp) {
-            const int ks0 = grp * GK;                              // 0..35 K, 36..67 V
-            if (grp + 1 < (DQK + DV) / 16 / GK) {
-#pragma unroll
-                for (int e = 0; e < GK; ++e) {
-                    const int ks = ks0 + GK + e;
-                    gnext[e] = ks < DQK / 16 ? gload(krs, kbq, ks) : gload(vrs, kbv, ks - DQK / 16);
-                }
+            for (int e = 0; e < GK; ++e) {
+                const int ks = grp * GK + e;
+                dst[e] = ks < DQK / 16 ? gload(krs, kbq, ks) : gload(vrs, kbv, ks - DQK / 16);
             }
+        };
+#pragma unroll
+        for (int g0 = 0; g0 < PF; ++g0) gissue(g0, gb[g0]);
+#pragma unroll
+        for (int grp = 0; grp < NG; ++grp) {
+            const int ks0 = grp * GK;                              // 0..35 K, 36..67 V
+            if (grp + PF < NG) gissue(grp + PF, gb[(grp + PF) % (PF + 1)]);
+            bf16x8* gcur = gb[grp % (PF + 1)];
 #pragma unroll
             for (int e = 0; e < GK; ++e) {
                 const int ks = ks0 + e;
@@ -434,8 +438,6 @@ void sbwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int e = 0; e < GK; ++e) gcur[e] = gnext[e];
         }
         // ---- P = exp(scale S - L) (0 for absent slots), dS = P (dP - D); the
         //      slot's bounds sum_h |P| max|dO_h| and sum_h |dS| max|Q_h|
@@ -574,14 +576,21 @@ void sbwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
 // ----------------------------------------------------------------------------
 // dQ_i = scale * dS_i K_I per (query row, head group).  Chunks of 32 slots:
 // the dS^T rows (stored by the kernel above in this LDS layout) and the
-// gathered K rows are copied into an LDS double buffer one chunk ahead; both
-// operands come from transposing reads.  Wave w owns head block w & 1 and
-// 9 of the 18 column blocks of d_qk.
+// gathered K rows are copied into a ring of DQ_NST LDS stages, two chunks
+// ahead of the products; both operands come from transposing reads.  The
+// row's keys are read once into LDS, so that no global load sits between the
+// stage copies (a wait for it would wait for every copy issued before it).
+// Wave w owns head block w & 1 and 9 of the 18 column blocks of d_qk.
 // ----------------------------------------------------------------------------
 constexpr int DQ_CH = 32;                        // slots per chunk
 constexpr int DQ_DS = DQ_CH * HG * 2;            // bytes of dS^T per chunk (4 KiB)
 constexpr int DQ_K = DQ_CH * QROW;               // bytes of K per chunk (40 KiB)
 constexpr int DQ_STAGE = DQ_DS + DQ_K;
+constexpr int DQ_NST = 3;                        // stages in the ring
+constexpr int DQ_MAXT = 1024;                    // slots whose keys the LDS list holds
+constexpr int DQ_KEYS = DQ_NST * DQ_STAGE;       // LDS offset of the key list
+constexpr int DQ_SMEM = DQ_KEYS + DQ_MAXT * 4;
+constexpr int DQ_STAGE_VM = 1 + 2 * 8;           // buffer -> LDS copies one stage issues per wave
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void sbwd_dq_kernel(const __bf16* __restrict__ K, const __bf16* __restrict__ dsw,
@@ -601,48 +610,86 @@ void sbwd_dq_kernel(const __bf16* __restrict__ K, const __bf16* __restrict__ dsw
     const size_t rowg = (size_t)i * G + hg;
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(K, Nkv * DQK * 2);
     const __amdgpu_buffer_rsrc_t drs = make_rsrc(dsw + rowg * (size_t)tpad * HG, tpad * HG * 2);
+    int* keys = reinterpret_cast<int*>(smem + DQ_KEYS);
 
-    // chunk c into stage buf: dS^T (4 x 1 KiB, one per wave), K rows 8 w .. + 7
+    // keys of the row's slots s0 .. s0 + DQ_MAXT - 1 (Nkv for an absent slot:
+    // a row past K's end, which the copies read as zeros)
+    auto load_keys = [&](int s0) {
+        for (int s = threadIdx.x; s < DQ_MAXT; s += 256) {
+            const int k = slot_key(irow, s0 + s, nval, Nkv);
+            keys[s] = k < 0 ? Nkv : k;
+        }
+    };
+    // chunk c into stage buf: dS^T (4 x 1 KiB, one per wave), K rows 8 w .. + 7.
+    // The loop's LDS reads are issued from assembly with explicit waits: the
+    // compiler would otherwise wait for every copy in flight before each one.
     auto stage = [&](int c, int buf) {
         char* st = smem + buf * DQ_STAGE;
         bdma16(drs, c * DQ_DS + w * 1024 + lane * 16, st + w * 1024);
-        const int key_lane = (lane < DQ_CH) ? slot_key(irow, c * DQ_CH + lane, nval, Nkv) : -1;
+        u32x4 kv[2];
+        const uint32_t ka = lds_addr(keys + (c * DQ_CH) % DQ_MAXT + w * 8);
+        lds_ld<0>(kv[0], ka);
+        lds_ld<16>(kv[1], ka);
+        lgkm_wait<0>(kv[0], kv[1]);
 #pragma unroll
         for (int rr = 0; rr < 8; ++rr) {
-            const int r = w * 8 + rr;
-            int key = __builtin_amdgcn_readlane(key_lane, r);
-            key = key < 0 ? Nkv : key;
-            stage_qrow(krs, key * (DQK * 2), st + DQ_DS, r, lane);
+            const int key = __builtin_amdgcn_readfirstlane((int)kv[rr >> 2][rr & 3]);
+            stage_qrow(krs, key * (DQK * 2), st + DQ_DS, w * 8 + rr, lane);
         }
     };
 
     f32x16 acc[9];
 #pragma unroll
     for (int b = 0; b < 9; ++b) acc[b] = zero16();
-    if (nch > 0) stage(0, 0);
+    load_keys(0);
     __syncthreads();
+    constexpr int CPL = DQ_MAXT / DQ_CH;         // chunks per key-list piece
+    for (int c = 0; c < DQ_NST - 1 && c < nch && c < CPL; ++c) stage(c, c);
     for (int c = 0; c < nch; ++c) {
-        const int buf = c & 1;
-        if (c + 1 < nch) stage(c + 1, buf ^ 1);
-        const char* st = smem + buf * DQ_STAGE;
+        // stage c has landed (for every wave after the barrier) and every
+        // wave is done with the stage the next copy overwrites
+        if (c + 1 < nch && (c + 1) % CPL != 0)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DQ_STAGE_VM) : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        const int cn = c + DQ_NST - 1;           // within this piece of the key list only
+        if (cn < nch && cn / CPL == c / CPL) stage(cn, cn % DQ_NST);
+        const char* st = smem + (c % DQ_NST) * DQ_STAGE;
         const __bf16* dsT = reinterpret_cast<const __bf16*>(st);
         const char* kt = st + DQ_DS;
 #pragma unroll
         for (int k4 = 0; k4 < 2; ++k4) {
-            // A: dS[m = head][k = slot], slots 16 k4 + 4 g + s4 (+ 8)
+            // A: dS[m = head][k = slot], slots 16 k4 + 4 g + s4 (+ 8); B: the K
+            // rows of the same slots, column block db0 + b; B reads run up to
+            // five blocks ahead of the products
             const int sr = 16 * k4 + 4 * g + s4;
             const int u = 8 * hb + 4 * hh + (t16 & 3);
-            const bf16x8 a = cat44(lds_read_tr(dsT + dsoff(sr, u)), lds_read_tr(dsT + dsoff(sr + 8, u)));
-#pragma unroll
-            for (int b = 0; b < 9; ++b) {
+            u32x2 a0, a1, bb[9][2];
+            tr_read2o<0>(a0, a1, lds_addr(dsT + dsoff(sr, u)), lds_addr(dsT + dsoff(sr + 8, u)));
+            auto issue_b = [&](int b) {
                 const int col = 32 * (db0 + b) + 16 * hh + 4 * (t16 & 3);
-                const bf16x8 bop = cat44(
-                    lds_read_tr(reinterpret_cast<const __bf16*>(kt + loff<QROW>(sr, col))),
-                    lds_read_tr(reinterpret_cast<const __bf16*>(kt + loff<QROW>(sr + 8, col))));
-                acc[b] = mfma32(a, bop, acc[b]);
-            }
+                tr_read2o<0>(bb[b][0], bb[b][1], lds_addr(kt + loff<QROW>(sr, col)),
+                             lds_addr(kt + loff<QROW>(sr + 8, col)));
+            };
+#pragma unroll
+            for (int b = 0; b < 5; ++b) issue_b(b);
+            static_for<0, 9>([&](auto bI) {
+                constexpr int b = decltype(bI)::value;
+                constexpr int after = (b + 4 < 8 ? b + 4 : 8) - b;   // B pairs issued after this one
+                lgkm_wait<2 * after>(a0, a1, bb[b][0]);
+                lgkm_wait<2 * after>(bb[b][1]);
+                acc[b] = mfma32(cat_u(a0, a1), cat_u(bb[b][0], bb[b][1]), acc[b]);
+                if constexpr (b + 5 < 9) issue_b(b + 5);
+            });
         }
-        __syncthreads();
+        if ((c + 1) % CPL == 0 && c + 1 < nch) {
+            // the next piece of the key list, then the ring refilled from it
+            __syncthreads();
+            load_keys((c + 1) * DQ_CH);
+            __syncthreads();
+            for (int cc = c + 1; cc < c + DQ_NST && cc < nch; ++cc) stage(cc, cc % DQ_NST);
+        }
     }
     // dQ: C[m = head][n = column]
 #pragma unroll
@@ -928,7 +975,7 @@ hipError_t launch_sparse_bwd(const void* q, const void* k, const void* v, const 
     }
     if ((long long)Nq * G > 0) {
         constexpr int smem_main = sp::BwdSmem::bytes;
-        constexpr int smem_dq = 2 * sp::DQ_STAGE;
+        constexpr int smem_dq = sp::DQ_SMEM;
         if ((e = hipFuncSetAttribute((const void*)sp::sbwd_main_kernel,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, smem_main)) != hipSuccess)
             return e;

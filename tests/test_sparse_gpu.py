@@ -9,6 +9,8 @@ d = 512, attn_sparse_bwd) against the fp64 oracle on the same seeded inputs.
 * reproducibility (no floating-point atomics);
 * index lists in any order and with a key repeated within a row (a gather:
   a repeated key counts as often as it is named);
+* index lists longer than 1024 slots (the dQ kernel reloads its key list and
+  refills its copy ring mid-row);
 * the full 64-head N = 4096 top-512 workload in the benchmark's launch
   configuration: every element of O, L, D, dQ, dK and dV.
 """
@@ -124,6 +126,23 @@ def test_sparse_unsorted_and_repeated_keys(lib, cfg):
     inp, n_rep = _shuffled_with_repeats(make_sparse_inputs(cfg), cfg, seed=7)
     say(f"[sparse] {cfg.name} unsorted lists, {n_rep} rows with a repeated key")
     _compare(_gpu(lib, inp, cfg), _oracle(inp, cfg, inp["topk_len"]))
+
+
+def test_sparse_long_index_lists(lib):
+    """Index lists longer than the 1024 slots whose keys the dQ kernel holds
+    at once (it reloads them and refills its copy ring mid-row): rows of 1100,
+    1031, 1024 and 700 valid slots drawn from 1300 keys without the causal
+    structure, the rest of each row -1."""
+    cfg = SparseConfig("sp_long", 64, 6, 1300, 576, 512, 1100, seed=14)
+    inp = make_sparse_inputs(cfg.with_(topk=1))       # Q, K, V, dO; the lists follow
+    rng = np.random.default_rng(cfg.seed)
+    lens = np.array([1100, 1031, 1024, 700, 1100, 1057], dtype=np.int32)
+    idx = np.full((cfg.Nq, cfg.topk), -1, dtype=np.int32)
+    for i, n in enumerate(lens):
+        idx[i, :n] = rng.choice(cfg.Nkv, n, replace=False)
+    inp = dict(inp, idx=idx, topk_len=lens)
+    say(f"[sparse] {cfg.name} Hq{cfg.Hq} Nq{cfg.Nq} Nkv{cfg.Nkv} topk{cfg.topk}, lists {lens.tolist()}")
+    _compare(_gpu(lib, inp, cfg), _oracle(inp, cfg, lens))
 
 
 def test_sparse_deterministic(lib):
