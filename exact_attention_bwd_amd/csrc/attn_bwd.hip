@@ -544,8 +544,14 @@ __device__ __forceinline__ void dkdv_w64_item(char* smem, const __bf16* __restri
     constexpr int DB = HD / 32;                  // 4 column blocks
     constexpr int TILE_EL = BR * HD;
 
-    const int lane = threadIdx.x & 63;
-    const int w = wave_id();
+    // FUSED: the item runs inside the persistent kernel's loop, and the
+    // register file is full inside the tile loop; lane, wave and N are
+    // recomputed here (and the per-tile copy offsets and the mask lanes where
+    // they are used) so that nothing derived from them is hoisted out of the
+    // item loop and held across it, which would spill inside the tile loop
+    const int lane = FUSED ? lane_here() : (int)(threadIdx.x & 63);
+    const int w = FUSED ? here_s(wave) : wave_id();
+    if (FUSED) N = here_s(N);
     const int l32 = lane & 31;
     const int g = lane >> 5;
     const int t16 = lane & 15;
@@ -579,8 +585,7 @@ __device__ __forceinline__ void dkdv_w64_item(char* smem, const __bf16* __restri
 
     // ---- K_j, V_j into LDS; then K_j into registers and the K image
     constexpr int ROWB = HD * 2;
-    int vo_q[BR * (HD / 8) / 64 / NW2], vo_k[BC2 * (HD / 8) / 64 / NW2];
-    stage_offsets<HD, BR, NW2>(vo_q, w, lane);
+    int vo_k[BC2 * (HD / 8) / 64 / NW2];
     stage_offsets<HD, BC2, NW2>(vo_k, w, lane);
     {
         const int rows = min(N - k0, BC2);
@@ -622,6 +627,8 @@ __device__ __forceinline__ void dkdv_w64_item(char* smem, const __bf16* __restri
         const int bytes = min(N - q0, BR) * ROWB;
         const size_t qhd = (size_t)(hq0 + gq) * N * HD;
         const size_t qst = (size_t)(hq0 + gq) * n_pad;
+        int vo_q[BR * (HD / 8) / 64 / NW2];
+        stage_offsets<HD, BR, NW2>(vo_q, FUSED ? here_s(w) : w, FUSED ? lane_here() : lane);
         stage_rows_b<HD, BR, NW2>(make_rsrc(Q + qhd + (size_t)q0 * HD, bytes), vo_q,
                                   smem + S::off_q + buf * S::TILE, w);
         stage_rows_b<HD, BR, NW2>(make_rsrc(dO + qhd + (size_t)q0 * HD, bytes), vo_q,
@@ -758,10 +765,11 @@ __device__ __forceinline__ void dkdv_w64_item(char* smem, const __bf16* __restri
                 const int kb0 = kw0 + 32 * kb;
                 const bool need_mask = (kb0 + 32 > N) || (CAUSAL && (kb0 + 31 > q0 + 32 * qb));
                 if (__builtin_expect(need_mask, 0)) {
-                    const int key = kb0 + l32;
+                    const int lm = FUSED ? lane_here() : lane;
+                    const int key = kb0 + (lm & 31);
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const int q = q0 + 32 * qb + (r >> 2) * 8 + g * 4 + (r & 3);
+                        const int q = q0 + 32 * qb + (r >> 2) * 8 + (lm >> 5) * 4 + (r & 3);
                         const bool masked = (key >= N) || (CAUSAL && key > q);
                         s[kb][r] = masked ? -__builtin_inff() : s[kb][r];
                     }
@@ -1387,29 +1395,33 @@ __device__ __forceinline__ void fused_item(char* smem, const FusedArgs& a, int b
     fused_dq_phase(smem, a.Kimg, a.dSw, a.dQ, bh, 4 * j, a.N, a.scale, wave);
 }
 
-// One item per workgroup: the workgroup claims the next ticket of its XCD's
-// queue when it starts, so tickets are taken in dispatch order and every
-// item an item waits for belongs to a workgroup that started earlier (and
-// runs, or is done).  The grid has as many workgroups per XCD as the
-// largest queue has items; surplus workgroups find their queue empty and
-// exit.  The workgroups check in as they finish (ctrl[8]).
+// Persistent (P4 Chapter 14, "Persistent"): about one workgroup per CU, each
+// claiming tickets of its XCD's queue one after another until the queue is
+// empty.  An item only waits for items with smaller tickets of the same
+// queue, which some workgroup claimed earlier and runs (or has finished), so
+// every wait ends.  The workgroups check in as they exit (ctrl[8]).
 __global__ __attribute__((amdgpu_flat_work_group_size(NW2 * 64, NW2 * 64), amdgpu_waves_per_eu(1, 1)))
 void bwd_fused_kernel(FusedArgs args) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int wave = wave_id();
-    int bh = 0, j = 0;
-    bool valid = false;
-    if (fused_claim(smem, args, xcc_id(), wave, bh, j, valid) && valid) fused_item(smem, args, bh, j, wave);
+    const int q = xcc_id();
+    for (;;) {
+        int bh = 0, j = 0;
+        bool valid = false;
+        if (!fused_claim(smem, args, q, here_s(wave), bh, j, valid)) break;
+        if (valid) fused_item(smem, args, bh, j, here_s(wave));
+    }
     if (wave == 0 && lane_here() == 0)
         __hip_atomic_fetch_add(args.ctrl + 8, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Runs after bwd_fused_kernel, as one workgroup: any ticket still unclaimed
-// (a queue whose XCD ran fewer workgroups than it has items) is taken here,
-// in queue order, so its items' reads of dS see either this workgroup's own
-// stores or those of the kernel before (complete at the kernel boundary).
-// Normally every queue is already exhausted and this returns at once.  The
-// item runs behind a call so that the loop does not hold its registers.
+// (a queue whose XCD got no workgroup of the kernel, on a device whose
+// workgroups are not dealt to all eight XCDs) is taken here, in queue order,
+// so its items' reads of dS see either this workgroup's own stores or those
+// of the kernel before (complete at the kernel boundary).  Normally every
+// queue is already exhausted and this returns at once.  The item runs behind
+// a call so that the loop does not hold its registers.
 __device__ __noinline__ void fused_item_call(char* smem, const FusedArgs* a, int bh, int j, int wave) {
     FusedArgs u;
     u.Q = uni(a->Q); u.K = uni(a->K); u.V = uni(a->V); u.dO = uni(a->dO); u.Lb = uni(a->Lb); u.Dp = uni(a->Dp);
@@ -1594,13 +1606,19 @@ static hipError_t launch_fused(const void* q, const void* k, const void* v, cons
     }
     bwd::FusedArgs a{(const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dO, Lb, Dp, dSw, kimg,
                      (__bf16*)dq, (__bf16*)dk, (__bf16*)dv, ctrl, BH, H, N, n_pad, scale};
-    // queue 0 holds the most heads (ceil(BH / 8)), taken in pairs
+    // one workgroup per CU (LDS allows no more), as many per XCD as the
+    // largest queue has items at most; queue 0 holds the most heads
+    // (ceil(BH / 8)), taken in pairs
     const int tc2 = (N + bwd::BC2 - 1) / bwd::BC2;
     const int nq0 = (BH + 7) / 8;
     const int per_xcd = (nq0 + 1) / 2 * 2 * tc2;
     hipError_t e;
+    int dev = 0, cus = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+    if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    const int grid = std::min(8 * per_xcd, std::max(8, cus / 8 * 8));
     if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd::bwd_fused_kernel, dim3(8 * per_xcd), dim3(bwd::NW2 * 64), bwd::FusedSmem::bytes, stream, a);
+    hipLaunchKernelGGL(bwd::bwd_fused_kernel, dim3(grid), dim3(bwd::NW2 * 64), bwd::FusedSmem::bytes, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(bwd::bwd_fused_sweep_kernel, dim3(1), dim3(bwd::NW2 * 64), bwd::FusedSmem::bytes, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;

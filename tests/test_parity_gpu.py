@@ -203,13 +203,13 @@ def test_caller_stream_is_used(lib):
 
 @pytest.mark.parametrize("B,H,N", [(1, 3, 333), (8, 16, 4096), (1, 1, 129)])
 def test_fused_control_block(lib, B, H, N):
-    """The causal d = 128 backward runs as one kernel whose work queues and
-    progress flags sit at the start of the workspace (then a one-workgroup
-    sweep kernel).  After a call: every item published its last query tile
-    (4 j for key tile j), no wait reached its bound, every workgroup checked
-    in, each queue's ticket counter ran one past its workgroups (the sweep's
-    last claim), and the sweep found nothing left (each XCD ran enough
-    workgroups for its queue)."""
+    """The causal d = 128 backward runs as one persistent kernel whose work
+    queues and progress flags sit at the start of the workspace (then a
+    one-workgroup sweep kernel).  After a call: every item published its last
+    query tile (4 j for key tile j), no wait reached its bound, every
+    workgroup checked in, each queue's ticket counter ran past its items by
+    one failed claim per workgroup of its XCD plus the sweep's, and the sweep
+    found nothing left."""
     import torch
     cfg = DenseConfig("ctrl", B, H, N, 128, True, seed=21)
     inp = make_dense_inputs(cfg)
@@ -220,13 +220,16 @@ def test_fused_control_block(lib, B, H, N):
     lib.attn_bwd(q, k, v, do, lse, D, True, cfg.scale, workspace=ws)
     torch.cuda.synchronize()
     tc2 = -(-N // 256)
-    nq0 = -(-(B * H) // 8)                      # heads of the largest queue, taken in pairs
-    per_xcd = (nq0 + 1) // 2 * 2 * tc2
-    ctrl = ws[: (64 + B * H * tc2) * 4].view(torch.int32).cpu().numpy()
-    say(f"  tickets {ctrl[:8].tolist()} finished {ctrl[8]} wait-bound {ctrl[9]} swept {ctrl[10]}")
-    assert ctrl[8] == 8 * per_xcd
+    BH = B * H
+    nq = [(BH - q + 7) // 8 if q < BH else 0 for q in range(8)]   # heads of queue q, taken in pairs
+    items = [(n + 1) // 2 * 2 * tc2 for n in nq]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    grid = min(8 * max(items), max(8, cus // 8 * 8))           # workgroups, dealt round-robin to the XCDs
+    ctrl = ws[: (64 + BH * tc2) * 4].view(torch.int32).cpu().numpy()
+    say(f"  grid {grid} tickets {ctrl[:8].tolist()} finished {ctrl[8]} wait-bound {ctrl[9]} swept {ctrl[10]}")
+    assert ctrl[8] == grid
     assert ctrl[9] == 0 and ctrl[10] == 0
-    assert np.all(ctrl[:8] == per_xcd + 1)
+    assert ctrl[:8].tolist() == [items[q] + grid // 8 + 1 for q in range(8)]
     prog = ctrl[64:].reshape(B * H, tc2)
     assert np.array_equal(prog, np.tile(4 * np.arange(tc2), (B * H, 1))), prog
 
