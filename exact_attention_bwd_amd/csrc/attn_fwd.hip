@@ -28,9 +28,6 @@
 #include "launch.hpp"
 #include "tiles.hpp"
 
-#ifndef FWD_RB
-#define FWD_RB 1
-#endif
 
 namespace attn {
 namespace fwd {
@@ -375,13 +372,16 @@ __device__ __forceinline__ void settle_o(f32x16 (&o)[RB][4]) {
         asm volatile("s_nop 15\n\ts_nop 15" : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[0][2]), "+a"(o[0][3]));
 }
 
-// RB = 2: 4 waves (one per SIMD), 64 rows each; RB = 1: 8 waves (two per
-// SIMD), 32 rows each.  Both cover a 256-row query tile.
+// One work item of the d = 128 forward: query tile qt (256 rows) of flattened
+// head bh.  RB = 2: 4 waves (one per SIMD), 64 rows each; RB = 1: 8 waves (two
+// per SIMD), 32 rows each.  Both cover a 256-row query tile.  On return every
+// wave has issued its last LDS read and its last copy has landed, but other
+// waves may still read LDS: the caller passes a barrier before the next item.
 template <bool CAUSAL, int RB>
-__global__ __attribute__((amdgpu_flat_work_group_size(512 / RB, 512 / RB), amdgpu_waves_per_eu(3 - RB, 3 - RB)))
-void fwd_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
-                    const __bf16* __restrict__ V, __bf16* __restrict__ O, float* __restrict__ Lse,
-                    int BH, int H, int G, int N, float scale) {
+__device__ __forceinline__ void fwd_w64_item(char* smem, const __bf16* __restrict__ Q,
+                                             const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+                                             __bf16* __restrict__ O, float* __restrict__ Lse, int H, int G,
+                                             int N, float scale, int bh, int qt) {
     constexpr int HD = 128;
     constexpr int NW = 8 / RB;                   // waves per workgroup
     constexpr int EPT = 32 * RB;                 // softmax elements per lane per key tile
@@ -391,7 +391,6 @@ void fwd_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     using S = WSmem;
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
-    extern __shared__ __attribute__((aligned(16))) char smem[];
 
     const int lane = threadIdx.x & 63;
     const int w = wave_id();
@@ -401,28 +400,6 @@ void fwd_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const int hh = (lane >> 4) & 1;
     const int s4 = t16 >> 2;
 
-    // Work order.  Causal: query tile qt sees 4 (qt + 1) key tiles, so the
-    // last tiles go first.  Workgroups are dealt round-robin over the 8 XCDs
-    // (hardware index b runs on XCD b % 8); each XCD takes every eighth head
-    // and works through them two at a time, longest tiles first within each
-    // pair, so that the few heads in flight on an XCD keep their K / V in its
-    // L2.  Other head counts: longest tiles first over all heads.
-    // Non-causal: the tiles of one head run on one XCD.
-    const int tq = (N + WBM - 1) / WBM;
-    int bh, qt;
-    if (CAUSAL && BH % 16 == 0) {
-        const int x = blockIdx.x % 8, t = blockIdx.x / 8;
-        const int grp = t / (2 * tq), r = t % (2 * tq);
-        qt = tq - 1 - r / 2;
-        bh = (2 * grp + (r & 1)) * 8 + x;
-    } else if (CAUSAL) {
-        bh = blockIdx.x % BH;
-        qt = tq - 1 - blockIdx.x / BH;
-    } else {
-        const int logical = xcd_remap(blockIdx.x, BH * tq);
-        bh = logical / tq;
-        qt = logical % tq;
-    }
     const int q0 = qt * WBM;
     const int qrows = min(N - q0, WBM);
     const int qw = 32 * RB * w;                  // this wave's first row in the tile
@@ -762,6 +739,52 @@ void fwd_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     });
 }
 
+// Persistent (P4 Chapter 14, "Persistent"): a fixed grid, a multiple of 8
+// workgroups dealt round-robin to the 8 XCDs, each workgroup walking a fixed
+// list of items.  Work order.  Causal: query tile qt sees 4 (qt + 1) key
+// tiles, so the last tiles go first.  Each XCD takes every eighth head and
+// works through them two at a time, longest tiles first within each pair, so
+// that the few heads in flight on an XCD keep their K / V in its L2: the
+// XCD's items are numbered in that order, and round m of its workgroups takes
+// items m G8 .. m G8 + G8 - 1 (G8 workgroups per XCD) in snake order, the
+// k-th workgroup the k-th item in even rounds and the (G8 - 1 - k)-th in odd
+// ones, so that the heavy and light tiles of the rounds even out over the
+// workgroups.  Other causal head counts: longest tiles first over all heads.
+// Non-causal: one item per workgroup, the tiles of one head on one XCD.
+template <bool CAUSAL, int RB>
+__global__ __attribute__((amdgpu_flat_work_group_size(512 / RB, 512 / RB), amdgpu_waves_per_eu(3 - RB, 3 - RB)))
+void fwd_w64_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+                    const __bf16* __restrict__ V, __bf16* __restrict__ O, float* __restrict__ Lse,
+                    int BH, int H, int G, int N, float scale) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int tq = (N + WBM - 1) / WBM;
+    const int items = BH * tq, per_xcd = (items + 7) / 8;
+    if constexpr (!CAUSAL) {
+        // equal items: one per workgroup (a loop would only add registers)
+        const int logical = xcd_remap(blockIdx.x, items);
+        fwd_w64_item<CAUSAL, RB>(smem, Q, K, V, O, Lse, H, G, N, scale, logical / tq, logical % tq);
+        return;
+    }
+    const int G8 = gridDim.x / 8, x = blockIdx.x % 8, k = blockIdx.x / 8;
+    for (int m = 0; m * G8 < per_xcd; ++m) {
+        const int local = m * G8 + ((m & 1) ? G8 - 1 - k : k);
+        const int item = local * 8 + x;          // the item's XCD is x, as its workgroup's
+        if (local >= per_xcd || item >= items) continue;
+        int bh, qt;
+        if (CAUSAL && BH % 16 == 0) {
+            const int t = item / 8;
+            const int grp = t / (2 * tq), r = t % (2 * tq);
+            qt = tq - 1 - r / 2;
+            bh = (2 * grp + (r & 1)) * 8 + x;
+        } else {
+            bh = item % BH;
+            qt = tq - 1 - item / BH;
+        }
+        fwd_w64_item<CAUSAL, RB>(smem, Q, K, V, O, Lse, H, G, N, scale, bh, qt);
+        __syncthreads();                         // every wave is done with the LDS slots
+    }
+}
+
 }  // namespace fwd
 
 template <int HD, bool CAUSAL>
@@ -779,12 +802,18 @@ template <bool CAUSAL>
 static hipError_t launch_fwd_w64(const void* q, const void* k, const void* v, void* o, float* lse,
                                  int BH, int H, int G, int N, float scale, hipStream_t stream) {
     using S = fwd::WSmem;
-    constexpr int RB = FWD_RB;
+    constexpr int RB = 1;                        // 8 waves of 32 rows (RB = 2 ran slower: one wave's issue bound it)
     auto kern = fwd::fwd_w64_kernel<CAUSAL, RB>;
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, S::bytes);
     if (e != hipSuccess) return e;
+    // causal: one workgroup per CU (LDS and registers allow no more), a
+    // multiple of 8; non-causal: one per item
     const int tq = (N + fwd::WBM - 1) / fwd::WBM;
-    hipLaunchKernelGGL(kern, dim3(BH * tq), dim3(512 / RB), S::bytes, stream, (const __bf16*)q,
+    int dev = 0, cus = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+    if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    const int grid = CAUSAL ? std::min((BH * tq + 7) / 8 * 8, std::max(8, cus / 8 * 8)) : BH * tq;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(512 / RB), S::bytes, stream, (const __bf16*)q,
                        (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, BH, H, G, N, scale);
     return hipGetLastError();
 }

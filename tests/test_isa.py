@@ -188,8 +188,11 @@ def test_no_vector_register_copies(isa, src, kernel):
             continue                             # scalar source
         from_v = any(k == "v" for k, _ in srcs)
         if m.group(1).startswith("v_mov") or m.group(1) == "v_pk_mov_b32":
-            if from_v and (kernel not in FUNCTIONS or any(last_asm.get(r) for r in srcs)):
-                bad.append(l.strip())            # a copy of a VGPR (functions: whose latest writer is asm)
+            # a copy of a VGPR that assembly fills somewhere in the body
+            # (functions: whose latest writer is assembly); copies of values
+            # the compiler computed itself (a loop's hoisted bases) are safe
+            if from_v and (srcs & asm_dst if kernel not in FUNCTIONS else any(last_asm.get(r) for r in srcs)):
+                bad.append(l.strip())
         elif first <= i < last and srcs & asm_dst:
             bad.append(l.strip())                # AGPR traffic among the products
         elif last <= i < settle and srcs & last_dst:
