@@ -81,7 +81,9 @@ size_t attn_bwd_workspace_bytes(int B, int H, int N, int d);
 
 /*
  * Exact workspace size of attn_bwd / attn_bwd_gqa for this shape and masking
- * (Hkv = H for attn_bwd): the row statistics L*log2(e) and D padded to the
+ * (Hkv = H for attn_bwd): on the causal d = 128 path with H = Hkv, a control
+ * block of 64 + B*H*ceil(N/256) ints (work-queue counters, status words, one
+ * progress word per 256-key tile); the row statistics L*log2(e) and D padded to the
  * 64-row query tile (2 x B*H*ceil(N/64)*64 fp32); one bf16 128 x 64 dS tile per
  * (batch*head, 64-row query tile i, 128-key tile j) -- for causal only the
  * tiles with j <= i/2, the lower triangle; a bf16 copy of K rearranged as
@@ -100,10 +102,11 @@ size_t attn_bwd_workspace_bytes_ex(int B, int H, int Hkv, int N, int d, int caus
  * tiles: each workgroup keeps its keys' dK and dV in registers over the query
  * tiles and stores every bf16 dS tile in `workspace`; dQ_i = scale *
  * sum_j dS_ij K_j is then reduced in fp32 registers, without atomics:
- *  - causal, d = 128, H = Hkv: in the same kernel, by the workgroup of the
- *    key tile on the diagonal of query tiles i, once the workgroups of the
- *    earlier key tiles of that head have stored their dS tiles of those rows
- *    (their progress is published in the workspace);
+ *  - causal, d = 128, H = Hkv: in the same, persistent kernel (about one
+ *    workgroup per CU, each taking work items from its XCD's queue), by the
+ *    item of the key tile on the diagonal of query tiles i, once the items of
+ *    the earlier key tiles of that head have stored their dS tiles of those
+ *    rows (their progress is published in the workspace);
  *  - otherwise: by a second, query-parallel kernel.
  * All launches are on `stream`.
  *   q, k, v, dO : bf16 [B, H, N, d], read only
