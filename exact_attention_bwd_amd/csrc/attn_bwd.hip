@@ -1025,7 +1025,7 @@ void bwd_dq_kernel(const __bf16* __restrict__ Kimg, const __bf16* __restrict__ d
             const bool ok = t2 == 0 || has_i1;
             const __amdgpu_buffer_rsrc_t r =
                 make_rsrc(dSw + dst_tile(bh, ok ? i0 + t2 : i0, jj, tr_count, tc, CAUSAL), ok ? DS_B : 0);
-            bdma16(r, dst_lds_chunk(Ib * 64 + lane) * 16, smem + st * STB + I * 1024);
+            bdma16_nt(r, dst_lds_chunk(Ib * 64 + lane) * 16, smem + st * STB + I * 1024);
         }
     };
     // K image loads from assembly: the compiler cannot follow which register
@@ -1146,11 +1146,14 @@ __device__ __forceinline__ int xcc_id() {
     return (int)(x & 7);
 }
 
-// Buffer -> LDS copy that misses the CU's L1 (the data was written by other
-// CUs of this XCD during this kernel).
+// Buffer -> LDS copy of dS that misses the CU's L1 (sc0: the data was written
+// by other CUs of this XCD during this kernel) and is non-temporal (nt): each
+// dS tile is read exactly once, and streaming it keeps the caches for the
+// Q / dO tiles and K images that several items share (2.8% faster at the
+// causal B8 H16 N4096 d128 shape than with sc0 alone, same results).
 __device__ __forceinline__ void bdma16_l2(__amdgpu_buffer_rsrc_t r, int voff, void* lds_base) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16,
-                                             voff, 0, 0, 1);
+                                             voff, 0, 0, 3);
 }
 
 // s_waitcnt vmcnt(N) tied to the four registers (one 64-key step of K image

