@@ -851,10 +851,14 @@ __device__ __forceinline__ void dkdv_w64_item(char* smem, const __bf16* __restri
                     constexpr int sk = m & 1, k4 = (m - 2) >> 1;
                     // non-temporal when a second kernel reads dS much
                     // later: the tiles should not push the shared Q / dO
-                    // out of L2.  FUSED reads them back within a few tiles.
+                    // out of L2.  FUSED: device scope (sc1), written through
+                    // to memory at once while the line stays in L2 for the
+                    // reads that come soon; the later ones find it in memory
+                    // and its eviction costs nothing (0.5% faster than a
+                    // plain write-back store, 3% faster than non-temporal).
                     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, da[sk][k4]), dsr,
                                                            dst_run(qb, w & 1, sk, k4) + lane * 16, 0,
-                                                           FUSED ? 0 : 2);
+                                                           FUSED ? 16 : 2);
                 }
                 mfma_a(dk[kb][t & 3], da[kb][t >> 2], cat_u(tb[t][0], tb[t][1]));
                 // the next half's L and Q operands, after the last wait
