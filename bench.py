@@ -750,7 +750,8 @@ def main(argv=None):
         "data": "synthetic",
         "config": {
             "workload": f"{'causal' if cfg.causal else 'non-causal'} attention backward "
-                        f"(preprocess + fused backward) B{B} H{H}"
+                        f"(preprocess + {'fused backward' if kname == 'bwd_fused_kernel' else 'dK/dV and dQ kernels'}) "
+                        f"B{B} H{H}"
                         + (f" Hkv{hkv} (grouped-query)" if gqa else "")
                         + f" N{N} d{d} bf16, seed {cfg.seed}",
             "B": B, "H": H, "N": N, "d": d, "causal": cfg.causal, "scale": cfg.scale,
