@@ -82,13 +82,12 @@ def dense_metric(cfg, hkv=None):
 
 
 # The kernel that dominates a dense step, and the share of the conventional
-# FLOP count it performs.  Causal d = 128 with one query head per K/V head:
-# the fused kernel forms all five products (S, dP, dV, dK, dQ); its timing
-# events also cover the one-workgroup sweep launched after it.  Otherwise the
-# dK/dV kernel forms S, dP, dV and dK (4 of the 5) and the dQ kernel the
-# fifth.
+# FLOP count it performs.  Causal d = 128 (grouped-query or not): the fused
+# kernel forms all five products (S, dP, dV, dK, dQ); its timing events also
+# cover the one-workgroup sweep launched after it.  Otherwise the dK/dV
+# kernel forms S, dP, dV and dK (4 of the 5) and the dQ kernel the fifth.
 def dominant_kernel(d, causal, gqa):
-    if d == 128 and causal and not gqa:
+    if d == 128 and causal:
         return "bwd_fused_kernel", 1.0
     if d == 128:
         return "bwd_dkdv_w64_kernel", 0.8

@@ -603,10 +603,13 @@ __device__ __forceinline__ void dkdv_w64_item(char* smem, const __bf16* __restri
             kreg[kb][ks] = lds_read16(KS + (ob0 ^ (ks * 16)) + (64 * w + 32 * kb) * HD);
     {
         // 128-key image tile jt = w >> 1 of this workgroup; 32 blocks of 1 KiB,
-        // 16 per wave
+        // 16 per wave.  One image per K / V head, written by part 0; FUSED:
+        // one per query head (hq0, the item's only query head), which the
+        // dQ phases of that head's later items read
         const int jt = w >> 1, jg = 2 * j + jt;
-        if (jg < tc && sp == 0) {
-            const __amdgpu_buffer_rsrc_t kr = make_rsrc(Kimg + kimg_tile(bh, jg, tc, HD), BC * HD * 2);
+        if (jg < tc && (FUSED || sp == 0)) {
+            const __amdgpu_buffer_rsrc_t kr =
+                make_rsrc(Kimg + kimg_tile(FUSED ? hq0 : bh, jg, tc, HD), BC * HD * 2);
 #pragma unroll
             for (int b = 0; b < 16; ++b) {
                 const int blk = (w & 1) * 16 + b;
@@ -1342,7 +1345,8 @@ struct FusedArgs {
     __bf16* dK;
     __bf16* dV;
     int* ctrl;
-    int BH, H, N, n_pad;
+    float* part;                                 // G > 1: fp32 dK / dV partials, one per query head
+    int BH, H, G, N, n_pad;
     float scale;
 };
 
@@ -1371,7 +1375,9 @@ __device__ __forceinline__ bool fused_claim(char* smem, const FusedArgs& a, int 
 
 // One item: the dK/dV loop of key tile j of head bh (publishing its
 // progress), then, once every item j' < j of the head has stored the dS
-// tiles of query tiles 4 j .. 4 j + 3, the dQ of those tiles.
+// tiles of query tiles 4 j .. 4 j + 3, the dQ of those tiles.  GQA: bh is a
+// query head of a group of G > 1 sharing one K / V head.
+template <bool GQA>
 __device__ __forceinline__ void fused_item(char* smem, const FusedArgs& a, int bh, int j, int wave) {
     const int tc2 = (a.N + BC2 - 1) / BC2;
     int* const st = reinterpret_cast<int*>(smem + FusedSmem::state);
@@ -1381,8 +1387,18 @@ __device__ __forceinline__ void fused_item(char* smem, const FusedArgs& a, int b
         st[5] = (int)(uint32_t)(slot >> 32);
     }
     __syncthreads();
-    dkdv_w64_item<true, true>(smem, a.Q, a.K, a.V, a.dO, a.Lb, a.Dp, a.dSw, a.Kimg, a.dK, a.dV, a.BH, a.H, 1, 1,
-                              nullptr, a.N, a.n_pad, a.scale, bh, j, nullptr, wave);
+    if constexpr (GQA) {
+        // query head bh is row (K / V head, part = its index in the group) of
+        // a dK/dV grid with one part per query head; its dK and dV go out as
+        // fp32 partials, which gqa_reduce_kernel sums over the group
+        const int G = here_s(a.G), H = a.H;
+        const int mapped = ((bh / H) * (H / G) + (bh % H) / G) * G + (bh % H) % G;
+        dkdv_w64_item<true, true>(smem, a.Q, a.K, a.V, a.dO, a.Lb, a.Dp, a.dSw, a.Kimg, a.dK, a.dV, a.BH, H, G,
+                                  G, a.part, a.N, a.n_pad, a.scale, mapped, j, nullptr, wave);
+    } else {
+        dkdv_w64_item<true, true>(smem, a.Q, a.K, a.V, a.dO, a.Lb, a.Dp, a.dSw, a.Kimg, a.dK, a.dV, a.BH, a.H, 1,
+                                  1, nullptr, a.N, a.n_pad, a.scale, bh, j, nullptr, wave);
+    }
     // its own stores are complete: the loop ended in a barrier after
     // waiting for them
     if (wave == 0 && lane_here() == 0) {
@@ -1407,6 +1423,7 @@ __device__ __forceinline__ void fused_item(char* smem, const FusedArgs& a, int b
 // empty.  An item only waits for items with smaller tickets of the same
 // queue, which some workgroup claimed earlier and runs (or has finished), so
 // every wait ends.  The workgroups check in as they exit (ctrl[8]).
+template <bool GQA>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW2 * 64, NW2 * 64), amdgpu_waves_per_eu(1, 1)))
 void bwd_fused_kernel(FusedArgs args) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -1416,7 +1433,7 @@ void bwd_fused_kernel(FusedArgs args) {
         int bh = 0, j = 0;
         bool valid = false;
         if (!fused_claim(smem, args, q, here_s(wave), bh, j, valid)) break;
-        if (valid) fused_item(smem, args, bh, j, here_s(wave));
+        if (valid) fused_item<GQA>(smem, args, bh, j, here_s(wave));
     }
     if (wave == 0 && lane_here() == 0)
         __hip_atomic_fetch_add(args.ctrl + 8, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1429,15 +1446,18 @@ void bwd_fused_kernel(FusedArgs args) {
 // of the kernel before (complete at the kernel boundary).  Normally every
 // queue is already exhausted and this returns at once.  The item runs behind
 // a call so that the loop does not hold its registers.
+template <bool GQA>
 __device__ __noinline__ void fused_item_call(char* smem, const FusedArgs* a, int bh, int j, int wave) {
     FusedArgs u;
     u.Q = uni(a->Q); u.K = uni(a->K); u.V = uni(a->V); u.dO = uni(a->dO); u.Lb = uni(a->Lb); u.Dp = uni(a->Dp);
     u.dSw = uni(a->dSw); u.Kimg = uni(a->Kimg); u.dQ = uni(a->dQ); u.dK = uni(a->dK); u.dV = uni(a->dV);
-    u.ctrl = uni(a->ctrl); u.BH = uni(a->BH); u.H = uni(a->H); u.N = uni(a->N); u.n_pad = uni(a->n_pad);
+    u.ctrl = uni(a->ctrl); u.part = uni(a->part); u.BH = uni(a->BH); u.H = uni(a->H); u.G = uni(a->G);
+    u.N = uni(a->N); u.n_pad = uni(a->n_pad);
     u.scale = uni(a->scale);
-    fused_item(uni(smem), u, uni(bh), uni(j), uni(wave));
+    fused_item<GQA>(uni(smem), u, uni(bh), uni(j), uni(wave));
 }
 
+template <bool GQA>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW2 * 64, NW2 * 64), amdgpu_waves_per_eu(1, 1)))
 void bwd_fused_sweep_kernel(FusedArgs args) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -1449,7 +1469,7 @@ void bwd_fused_sweep_kernel(FusedArgs args) {
             if (!valid) continue;
             if (wave == 0 && lane_here() == 0)
                 __hip_atomic_fetch_add(args.ctrl + 10, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            fused_item_call(smem, &args, bh, j, wave);
+            fused_item_call<GQA>(smem, &args, bh, j, wave);
         }
     }
 }
@@ -1517,21 +1537,25 @@ struct WsLayout {
     int n_ctrl;                                  // ints of the fused kernel's control block (0: none)
 };
 
-// The fused causal kernel serves d = 128 with one query head per K / V head.
-static bool use_fused(int G, int d, bool causal) { return causal && d == 128 && G == 1; }
+// The fused causal kernel serves d = 128; with grouped-query heads its items
+// are the query heads, each writing fp32 dK / dV partials (one part per query
+// head) that gqa_reduce_kernel sums over the group.
+static bool use_fused(int G, int d, bool causal) { (void)G; return causal && d == 128; }
 
 static WsLayout ws_layout(int BH, int G, int N, int d, bool causal) {
     WsLayout w{};
     const size_t rows = (size_t)BH * n_pad_of(N);
     const int tr = (N + bwd::BR - 1) / bwd::BR, tc = (N + bwd::BC - 1) / bwd::BC;
-    const int ns = gqa_parts(BH / G, N, d, G);
+    const bool fused = use_fused(G, d, causal);
+    const int ns = fused ? G : gqa_parts(BH / G, N, d, G);
     size_t o = 0;
-    w.n_ctrl = use_fused(G, d, causal) ? bwd::F_CTRL + BH * ((N + bwd::BC2 - 1) / bwd::BC2) : 0;
+    w.n_ctrl = fused ? bwd::F_CTRL + BH * ((N + bwd::BC2 - 1) / bwd::BC2) : 0;
     w.ctrl = o; o = align256(o + (size_t)w.n_ctrl * sizeof(int));
     w.lb = o;   o = align256(o + rows * sizeof(float));
     w.dp = o;   o = align256(o + rows * sizeof(float));
     w.ds = o;   o = align256(o + (size_t)BH * bwd::dst_tiles_per_head(tr, tc, causal) * bwd::DST_EL * 2);
-    w.kimg = o; o = align256(o + (size_t)(BH / G) * tc * bwd::BC * d * 2);
+    // K images: one per K / V head; the fused kernel keeps one per query head
+    w.kimg = o; o = align256(o + (size_t)(fused ? BH : BH / G) * tc * bwd::BC * d * 2);
     w.part = o; o = align256(o + (ns > 1 ? 2 * (size_t)ns * (BH / G) * N * d * sizeof(float) : 0));
     w.total = o;
     return w;
@@ -1603,16 +1627,22 @@ static hipError_t launch_pair(const void* q, const void* k, const void* v, const
     return launch_dq<HD, CAUSAL>(kimg, dSw, dq, BH, H, G, N, scale, stream);
 }
 
+// BH query heads, G of them per K / V head (G > 1: fp32 partials in `part`,
+// summed after the fused kernel)
 static hipError_t launch_fused(const void* q, const void* k, const void* v, const void* dO,
                                const float* Lb, const float* Dp, __bf16* dSw, __bf16* kimg, int* ctrl,
-                               void* dq, void* dk, void* dv, int BH, int H, int N, int n_pad, float scale,
-                               hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
-    for (const void* kern : {(const void*)bwd::bwd_fused_kernel, (const void*)bwd::bwd_fused_sweep_kernel}) {
+                               float* part, void* dq, void* dk, void* dv, int BH, int H, int G, int N,
+                               int n_pad, float scale, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+    const void* main_kern = G > 1 ? (const void*)bwd::bwd_fused_kernel<true> : (const void*)bwd::bwd_fused_kernel<false>;
+    const void* sweep_kern =
+        G > 1 ? (const void*)bwd::bwd_fused_sweep_kernel<true> : (const void*)bwd::bwd_fused_sweep_kernel<false>;
+    for (const void* kern : {main_kern, sweep_kern}) {
         hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bwd::FusedSmem::bytes);
         if (e != hipSuccess) return e;
     }
     bwd::FusedArgs a{(const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dO, Lb, Dp, dSw, kimg,
-                     (__bf16*)dq, (__bf16*)dk, (__bf16*)dv, ctrl, BH, H, N, n_pad, scale};
+                     (__bf16*)dq, (__bf16*)dk, (__bf16*)dv, ctrl, G > 1 ? part : nullptr, BH, H, G, N,
+                     n_pad, scale};
     // one workgroup per CU (LDS allows no more), as many per XCD as the
     // largest queue has items at most; queue 0 holds the most heads
     // (ceil(BH / 8)), taken in pairs
@@ -1625,11 +1655,23 @@ static hipError_t launch_fused(const void* q, const void* k, const void* v, cons
     if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
     const int grid = std::min(8 * per_xcd, std::max(8, cus / 8 * 8));
     if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd::bwd_fused_kernel, dim3(grid), dim3(bwd::NW2 * 64), bwd::FusedSmem::bytes, stream, a);
+    if (G > 1)
+        hipLaunchKernelGGL(bwd::bwd_fused_kernel<true>, dim3(grid), dim3(bwd::NW2 * 64), bwd::FusedSmem::bytes, stream, a);
+    else
+        hipLaunchKernelGGL(bwd::bwd_fused_kernel<false>, dim3(grid), dim3(bwd::NW2 * 64), bwd::FusedSmem::bytes, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd::bwd_fused_sweep_kernel, dim3(1), dim3(bwd::NW2 * 64), bwd::FusedSmem::bytes, stream, a);
+    if (G > 1)
+        hipLaunchKernelGGL(bwd::bwd_fused_sweep_kernel<true>, dim3(1), dim3(bwd::NW2 * 64), bwd::FusedSmem::bytes, stream, a);
+    else
+        hipLaunchKernelGGL(bwd::bwd_fused_sweep_kernel<false>, dim3(1), dim3(bwd::NW2 * 64), bwd::FusedSmem::bytes, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
+    if (G > 1) {
+        const long long n = (long long)(BH / G) * N * 128;
+        hipLaunchKernelGGL(gqa_reduce_kernel, dim3(grid_for(2 * n, 1024, 16384)), dim3(256), 0, stream,
+                           part, (__bf16*)dk, (__bf16*)dv, G, n);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     return hipSuccess;
 }
 
@@ -1653,8 +1695,8 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* d
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (use_fused(G, d, causal))
-        return launch_fused(q, k, v, dO, Lb, Dp, dSw, kimg, ctrl, dq, dk, dv, BH, H, N, n_pad, scale, stream,
-                            main_start, main_stop);
+        return launch_fused(q, k, v, dO, Lb, Dp, dSw, kimg, ctrl, part, dq, dk, dv, BH, H, G, N, n_pad, scale,
+                            stream, main_start, main_stop);
     if (d == 128)
         return causal ? launch_pair<128, true>(q, k, v, dO, Lb, Dp, dSw, kimg, part, dq, dk, dv, BH, H, G, N, n_pad, scale, stream, main_start, main_stop)
                       : launch_pair<128, false>(q, k, v, dO, Lb, Dp, dSw, kimg, part, dq, dk, dv, BH, H, G, N, n_pad, scale, stream, main_start, main_stop);

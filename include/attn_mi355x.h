@@ -81,15 +81,17 @@ size_t attn_bwd_workspace_bytes(int B, int H, int N, int d);
 
 /*
  * Exact workspace size of attn_bwd / attn_bwd_gqa for this shape and masking
- * (Hkv = H for attn_bwd): on the causal d = 128 path with H = Hkv, a control
- * block of 64 + B*H*ceil(N/256) ints (work-queue counters, status words, one
- * progress word per 256-key tile); the row statistics L*log2(e) and D padded to the
+ * (Hkv = H for attn_bwd): on the causal d = 128 path, a control block of
+ * 64 + B*H*ceil(N/256) ints (work-queue counters, status words, one progress
+ * word per query head and 256-key tile); the row statistics L*log2(e) and D padded to the
  * 64-row query tile (2 x B*H*ceil(N/64)*64 fp32); one bf16 128 x 64 dS tile per
  * (batch*head, 64-row query tile i, 128-key tile j) -- for causal only the
  * tiles with j <= i/2, the lower triangle; a bf16 copy of K rearranged as
- * matrix-core operands (B*Hkv*ceil(N/128)*128*d*2 bytes); and, for grouped-
- * query shapes whose query heads are split over several workgroups, fp32
- * partials of dK and dV.  Each part is rounded up to 256 bytes.  0 when
+ * matrix-core operands (B*Hkv*ceil(N/128)*128*d*2 bytes; on the causal
+ * d = 128 path one copy per query head, B*H*...); and, for grouped-query
+ * shapes whose query heads are split over several workgroups (on the causal
+ * d = 128 path: every query head its own part), fp32 partials of dK and dV
+ * (2*parts*B*Hkv*N*d*4 bytes).  Each part is rounded up to 256 bytes.  0 when
  * B*H*N == 0 or the shape is unsupported.
  */
 size_t attn_bwd_workspace_bytes_ex(int B, int H, int Hkv, int N, int d, int causal);
@@ -102,11 +104,11 @@ size_t attn_bwd_workspace_bytes_ex(int B, int H, int Hkv, int N, int d, int caus
  * tiles: each workgroup keeps its keys' dK and dV in registers over the query
  * tiles and stores every bf16 dS tile in `workspace`; dQ_i = scale *
  * sum_j dS_ij K_j is then reduced in fp32 registers, without atomics:
- *  - causal, d = 128, H = Hkv: in the same, persistent kernel (about one
- *    workgroup per CU, each taking work items from its XCD's queue), by the
- *    item of the key tile on the diagonal of query tiles i, once the items of
- *    the earlier key tiles of that head have stored their dS tiles of those
- *    rows (their progress is published in the workspace);
+ *  - causal, d = 128: in the same, persistent kernel (about one workgroup per
+ *    CU, each taking work items from its XCD's queue), by the item of the key
+ *    tile on the diagonal of query tiles i, once the items of the earlier key
+ *    tiles of that head have stored their dS tiles of those rows (their
+ *    progress is published in the workspace);
  *  - otherwise: by a second, query-parallel kernel.
  * All launches are on `stream`.
  *   q, k, v, dO : bf16 [B, H, N, d], read only
@@ -154,8 +156,10 @@ attn_status attn_bwd_timed(const void* q, const void* k, const void* v, const vo
  * Shapes: q, o, dO, dq  [B, H, N, d];  k, v, dk, dv  [B, Hkv, N, d];
  * lse, D fp32 [B, H, N].  Hkv must divide H (ATTN_ERR_INVALID_ARG otherwise);
  * everything else as for attn_fwd / attn_bwd, which are these calls with
- * Hkv = H.  The per-head sums of dK and dV are accumulated in registers in a
- * fixed order (no atomics): results are bitwise reproducible.
+ * Hkv = H.  The per-head sums of dK and dV are formed in fp32 in a fixed
+ * order, in registers or as one partial per workgroup added by a reduction
+ * kernel (causal d = 128: the fused kernel's items are the query heads, one
+ * partial each); no atomics, so results are bitwise reproducible.
  */
 attn_status attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                          int H, int Hkv, int N, int d, int causal, float scale, void* stream);
@@ -171,8 +175,9 @@ attn_status attn_bwd_gqa(const void* q, const void* k, const void* v, const void
                          void* workspace, size_t workspace_bytes, int B, int H, int Hkv, int N,
                          int d, int causal, float scale, void* stream);
 
-/* attn_bwd_gqa with the dK/dV kernel bracketed by main_start / main_stop, as
- * attn_bwd_timed. */
+/* attn_bwd_gqa with the dominant kernel bracketed by main_start / main_stop,
+ * as attn_bwd_timed (the fused kernel and its sweep on the causal d = 128
+ * path, the dK/dV kernel otherwise; the group reduction falls outside). */
 attn_status attn_bwd_gqa_timed(const void* q, const void* k, const void* v, const void* dO,
                                const float* lse, const float* D, void* dq, void* dk, void* dv,
                                void* workspace, size_t workspace_bytes, int B, int H, int Hkv, int N,

@@ -4,8 +4,9 @@ through the C ABI against the fp64 oracle (``oracle.gqa_forward`` /
 O, L, D, dQ per query head and dK, dV per K/V head (summed over the query
 heads that share it).  Cases cover d = 64 and 128, causal and not, ragged
 lengths over several tiles, MQA (Hkv = 1) and G = 1 through the grouped entry
-points, plus a full-length causal case (N = 4096) with the group sums of the
-first and last K/V head checked against the oracle.
+points, plus full-length cases (N = 4096) through the fused kernel and
+through the separate dK/dV and dQ kernels, with the group sums of the first
+and last K/V head checked against the oracle.
 """
 import numpy as np
 import pytest
@@ -52,11 +53,15 @@ def test_gqa_end_to_end(lib, cfg, hkv):
 
 
 FULL = [
-    # one K/V head's 8 query heads split over 8 workgroups (fp32 partials)
+    # causal d = 128 runs the fused kernel, one item per (query head, key
+    # tile), each writing fp32 dK / dV partials that the group reduction sums:
+    # 8 query heads per K/V head, then 4 with many K/V heads
     (DenseConfig("gqa8_c128_4k", 1, 16, 4096, 128, True, seed=27), 2),
-    # 4 query heads per K/V head: two per workgroup at d = 128 (two partials),
-    # all four in one workgroup at d = 64 (no partials)
     (DenseConfig("gqa4_c128_b8", 8, 32, 4096, 128, True, seed=28), 8),
+    # the separate dK/dV and dQ kernels: 4 query heads per K/V head, two per
+    # workgroup at d = 128 (two partials), all four in one workgroup at d = 64
+    # (no partials)
+    (DenseConfig("gqa4_n128_b8", 8, 32, 4096, 128, False, seed=30), 8),
     (DenseConfig("gqa4_n64_b8", 8, 32, 4096, 64, False, seed=29), 8),
 ]
 

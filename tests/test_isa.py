@@ -38,8 +38,10 @@ import pytest
 from exact_attention_bwd_amd import build as B
 
 KERNELS = (
-    ("attn_bwd.hip", "_ZN4attn3bwd16bwd_fused_kernel"),
-    ("attn_bwd.hip", "_ZN4attn3bwd15fused_item_call"),
+    ("attn_bwd.hip", "_ZN4attn3bwd16bwd_fused_kernelILb0E"),
+    ("attn_bwd.hip", "_ZN4attn3bwd16bwd_fused_kernelILb1E"),
+    ("attn_bwd.hip", "_ZN4attn3bwd15fused_item_callILb0E"),
+    ("attn_bwd.hip", "_ZN4attn3bwd15fused_item_callILb1E"),
     ("attn_bwd.hip", "_ZN4attn3bwd19bwd_dkdv_w64_kernelILb1E"),
     ("attn_bwd.hip", "_ZN4attn3bwd19bwd_dkdv_w64_kernelILb0E"),
     ("attn_bwd.hip", "_ZN4attn3bwd13bwd_dq_kernelILi128ELb1E"),
@@ -106,7 +108,7 @@ STORE = re.compile(r"^\s*(ds_write|buffer_store|global_store|flat_store|scratch_
 IMM = re.compile(r"^-?(0x[0-9a-f]+|\d+(\.\d+)?)$")
 
 
-FUNCTIONS = ("_ZN4attn3bwd15fused_item_call",)
+FUNCTIONS = ("_ZN4attn3bwd15fused_item_callILb0E", "_ZN4attn3bwd15fused_item_callILb1E")
 
 
 @pytest.mark.parametrize("src,kernel", KERNELS, ids=[k for _, k in KERNELS])
