@@ -92,3 +92,36 @@ def test_gqa_full_length_group_sums(lib, cfg, hkv):
             for n in ("o", "D", "dq"):
                 assert_close(f"{n}[{c * G + h}]", res[n][c * G + h], ref[n][0, h])
             assert_lse(res["lse"][c * G + h], ref["lse"][0, h])
+
+
+@pytest.mark.parametrize("B,H,hkv,N", [(1, 8, 2, 300), (8, 16, 2, 4096)])
+def test_gqa_fused_control_block(lib, B, H, hkv, N):
+    """Grouped-query causal d = 128 runs the persistent fused kernel with the
+    query heads as its items: after a call its control block shows what the
+    one-query-head-per-K/V-head case shows (every item published its last
+    query tile, no wait reached its bound, every workgroup checked in, each
+    queue's ticket counter ran one failed claim per workgroup of its XCD plus
+    the sweep's past its items, and the sweep found nothing left)."""
+    import torch
+    cfg = DenseConfig("gqa_ctrl", B, H, N, 128, True, seed=35)
+    say(f"[gqa-ctrl] B{B} H{H} Hkv{hkv} N{N}")
+    inp = make_gqa_inputs(cfg, hkv)
+    q, k, v, do = (to_dev(inp[n]) for n in ("q", "k", "v", "do"))
+    o, lse = lib.attn_fwd_gqa(q, k, v, True, cfg.scale)
+    D = lib.attn_bwd_preprocess(o, do)
+    ws = torch.empty(lib.attn_bwd_workspace_bytes(B, H, N, 128, True, hkv), dtype=torch.uint8, device="cuda")
+    lib.attn_bwd_gqa(q, k, v, do, lse, D, True, cfg.scale, workspace=ws)
+    torch.cuda.synchronize()
+    tc2 = -(-N // 256)
+    BH = B * H
+    nq = [(BH - qq + 7) // 8 if qq < BH else 0 for qq in range(8)]    # query heads of queue qq, in pairs
+    items = [(n + 1) // 2 * 2 * tc2 for n in nq]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    grid = min(8 * max(items), max(8, cus // 8 * 8))
+    ctrl = ws[: (64 + BH * tc2) * 4].view(torch.int32).cpu().numpy()
+    say(f"  grid {grid} tickets {ctrl[:8].tolist()} finished {ctrl[8]} wait-bound {ctrl[9]} swept {ctrl[10]}")
+    assert ctrl[8] == grid
+    assert ctrl[9] == 0 and ctrl[10] == 0
+    assert ctrl[:8].tolist() == [items[qq] + grid // 8 + 1 for qq in range(8)]
+    prog = ctrl[64:].reshape(BH, tc2)
+    assert np.array_equal(prog, np.tile(4 * np.arange(tc2), (BH, 1))), prog
