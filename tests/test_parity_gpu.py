@@ -103,6 +103,10 @@ RAGGED = [
     # an odd number of 64-row query tiles (the dQ kernel's last pair has one)
     DenseConfig("heads16_c128", 1, 16, 300, 128, True, seed=9),
     DenseConfig("heads32_c64", 2, 16, 200, 64, True, seed=10),
+    # the fused causal kernel at about twice the headline length, with a
+    # partial last 256-key tile: items walk up to 125 query tiles and the
+    # longest dQ phases run 126 steps of 64 keys
+    DenseConfig("long_c128", 1, 2, 8000, 128, True, seed=36),
 ]
 
 
