@@ -137,3 +137,30 @@ def test_sparse_backward_in_a_graph(lib):
                             dv=outs["dv"], workspace=ws)
 
     _replay_and_compare(eager, captured, outs)
+
+
+def test_grouped_query_backward_in_a_graph(lib):
+    """Causal d = 128 grouped-query heads: the fused kernel with fp32 partials
+    and the group reduction after it, captured together."""
+    import torch
+    from attn_inputs import make_gqa_inputs
+    cfg = DenseConfig("graph_gqa", 1, 8, 500, 128, True, seed=37)
+    hkv = 2
+    say(f"[graph] attn_bwd_gqa B{cfg.B} H{cfg.H} Hkv{hkv} N{cfg.N} causal")
+    inp = make_gqa_inputs(cfg, hkv)
+    q, k, v, do = (to_dev(inp[n]) for n in ("q", "k", "v", "do"))
+    o, lse = lib.attn_fwd_gqa(q, k, v, True, cfg.scale)
+    D = lib.attn_bwd_preprocess(o, do)
+    ws = torch.empty(lib.attn_bwd_workspace_bytes(cfg.B, cfg.H, cfg.N, cfg.d, True, hkv), dtype=torch.uint8,
+                     device="cuda")
+    outs = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v)}
+
+    def eager():
+        dq, dk, dv = lib.attn_bwd_gqa(q, k, v, do, lse, D, True, cfg.scale, workspace=ws)
+        return {"dq": dq, "dk": dk, "dv": dv}
+
+    def captured():
+        lib.attn_bwd_gqa(q, k, v, do, lse, D, True, cfg.scale, dq=outs["dq"], dk=outs["dk"], dv=outs["dv"],
+                         workspace=ws)
+
+    _replay_and_compare(eager, captured, outs)
