@@ -894,9 +894,17 @@ __device__ __forceinline__ void dkdv_w64_item(char* smem, const __bf16* __restri
     //      Element r of tile (kb, db) is key 32 kb + 8 (r / 4) + 4 g + r % 4
     //      of the wave, column 32 db + l32.
     if (NS > 1) {
-        // fp32 partials of part sp: the dK block, then the dV block
+        // fp32 partials of part sp (the dK block, then the dV block) through
+        // buffer resources over this wave's valid keys, laid out as the bf16
+        // stores below
         const size_t bkv = BH / NS, pb0 = ((size_t)sp * bkv + bh) * N * HD;
         const size_t pv = (size_t)NS * bkv * N * HD;
+        const int kwu = __builtin_amdgcn_readfirstlane(kw0);
+        const int nkb = __builtin_amdgcn_readfirstlane(max(0, min(64, N - kwu)) * HD * 4);
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(part + pb0 + (size_t)kwu * HD, nkb);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(part + pv + pb0 + (size_t)kwu * HD, nkb);
+        const int le = FUSED ? lane_here() : lane;
+        const int vo = (4 * (le >> 5) * HD + (le & 31)) * 4;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -904,12 +912,16 @@ __device__ __forceinline__ void dkdv_w64_item(char* smem, const __bf16* __restri
                 asm volatile("s_nop 15\n\ts_nop 7" : "+a"(dv[kb][db]), "+a"(dk[kb][db]));
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int key = kw0 + 32 * kb + (r >> 2) * 8 + g * 4 + (r & 3);
-                    if (key < N) {
-                        const size_t pb = pb0 + (size_t)key * HD + db * 32 + l32;
-                        part[pb] = dk[kb][db][r] * scale;
-                        part[pv + pb] = dv[kb][db][r];
-                    }
+                    const int so = (32 * kb + 8 * (r >> 2)) * HD * 4;
+                    const int io = ((r & 3) * HD + db * 32) * 4;
+                    // the dV element is moved to a vector register first: a
+                    // store straight from the accumulation register file came
+                    // out with one source register for all sixteen elements
+                    float x = dv[kb][db][r];
+                    asm volatile("" : "+v"(x));
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, dk[kb][db][r] * scale), rk,
+                                                          vo + io, so, 0);
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, x), rv, vo + io, so, 0);
                 }
             }
     } else {
