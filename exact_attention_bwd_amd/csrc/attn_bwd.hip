@@ -1430,11 +1430,13 @@ __device__ __forceinline__ void fused_item(char* smem, const FusedArgs& a, int b
     fused_dq_phase(smem, a.Kimg, a.dSw, a.dQ, bh, 4 * j, a.N, a.scale, wave);
 }
 
-// Persistent (P4 Chapter 14, "Persistent"): about one workgroup per CU, each
-// claiming tickets of its XCD's queue one after another until the queue is
-// empty.  An item only waits for items with smaller tickets of the same
-// queue, which some workgroup claimed earlier and runs (or has finished), so
-// every wait ends.  The workgroups check in as they exit (ctrl[8]).
+// Persistent (B200 attention blog, Chapter 14 "Persistent"): about one
+// workgroup per CU, each claiming tickets of its XCD's queue one after
+// another until the queue is empty.  An item only waits for items with
+// smaller tickets of the same queue, which some workgroup claimed earlier and
+// runs (or has finished), so every wait ends.  The workgroups check in as
+// they exit (ctrl[8]).  GQA: the items are query heads of groups sharing a
+// K / V head (dK / dV as fp32 partials).
 template <bool GQA>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW2 * 64, NW2 * 64), amdgpu_waves_per_eu(1, 1)))
 void bwd_fused_kernel(FusedArgs args) {

@@ -739,9 +739,9 @@ __device__ __forceinline__ void fwd_w64_item(char* smem, const __bf16* __restric
     });
 }
 
-// Persistent (P4 Chapter 14, "Persistent"): a fixed grid, a multiple of 8
-// workgroups dealt round-robin to the 8 XCDs, each workgroup walking a fixed
-// list of items.  Work order.  Causal: query tile qt sees 4 (qt + 1) key
+// Persistent (B200 attention blog, Chapter 14 "Persistent"): a fixed grid, a
+// multiple of 8 workgroups dealt round-robin to the 8 XCDs, each workgroup
+// walking a fixed list of items.  Work order.  Causal: query tile qt sees 4 (qt + 1) key
 // tiles, so the last tiles go first.  Each XCD takes every eighth head and
 // works through them two at a time, longest tiles first within each pair, so
 // that the few heads in flight on an XCD keep their K / V in its L2: the
