@@ -268,6 +268,12 @@ def profile_path(config, ext):
     return os.path.join(PROFILES, f"{config}_profile.{ext}")
 
 
+def profile_name(config, hkv):
+    """Name of a workload's profile: the config, plus the K/V head count for
+    grouped-query runs (a different kernel path than the config alone)."""
+    return config if hkv is None else f"{config}_hkv{hkv}"
+
+
 def copy_calibration():
     """A plain device-to-device copy of COPY_BYTES, three times: the copy kernel
     reads and writes exactly COPY_BYTES, which scales the TCC byte counters."""
@@ -344,7 +350,7 @@ def _trace_durations(d, last):
     return out
 
 
-def run_profile(out_dir, config, extra):
+def run_profile(out_dir, config, extra, name):
     """Kernel trace + counter passes of one workload, each under rocprofv3 in a
     child process of its own, then the per-kernel summary in profiles/."""
     out_dir = os.path.abspath(out_dir)
@@ -378,7 +384,7 @@ def run_profile(out_dir, config, extra):
                 return rc
     with open(os.path.join(out_dir, "meta.json"), "w") as f:
         json.dump(meta, f, indent=1)
-    summarise_profile(out_dir, config)
+    summarise_profile(out_dir, name)
     return 0
 
 
@@ -649,9 +655,9 @@ def main(argv=None):
 
     if args.profile:
         extra = [] if args.hkv is None else ["--hkv", str(args.hkv)]
-        return run_profile(args.profile, args.config, extra)
+        return run_profile(args.profile, args.config, extra, profile_name(args.config, args.hkv))
     if args.summarise:
-        summarise_profile(os.path.abspath(args.summarise), args.config)
+        summarise_profile(os.path.abspath(args.summarise), profile_name(args.config, args.hkv))
         return 0
 
     if args.copy_calibration:
@@ -773,7 +779,7 @@ def main(argv=None):
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(main_tf / PEAK_BF16_TFLOPS, 5),
-            "traffic": None if gqa else committed_traffic(cfg.name, kname),
+            "traffic": committed_traffic(profile_name(cfg.name, hkv if gqa else None), kname),
         },
         "sclk": clk.summary(),
         "context": ({"pages_rtx5090_v3_tflops": PAGES_BWD_TFLOPS,
